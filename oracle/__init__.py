@@ -1,0 +1,289 @@
+"""CPU oracle for 4-bit absmax block quantization and the W4 matmuls.
+
+TEST INFRASTRUCTURE ONLY: only tests/, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the HIP
+library (w4_gemm_amd) and neither imports the other.
+
+The quantizers and dequantizers are plain C (q4_oracle.c, fp32 steps exactly
+as each format is stated on the pages; see the header of that file for the
+passages and the readings).  The matmul references below are the plain
+definitions in fp64 on the oracle's own dequantized weights:
+
+  * W4A16 GEMV / GEMM: out[m, n] = sum_k a[m, k] * w'[n, k]  -- the matmul
+    the W4A16 scheme performs after dequantizing weights ("Low-bit inference
+    for very large MoE", table "Kernels on different hardware", row W4A16).
+  * W4A4 MXFP4: both operands MXFP4-quantized along K, then the same sum on
+    the dequantized values (same table, row W4A4).
+  * Grouped MoE GEMM: one low-bit weight matrix per expert, each routed row
+    multiplied by its expert's matrix (same page, "A few details", MoE
+    grouped GEMM bullet).
+
+numpy's fp64 matmul is the only library primitive used as a step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+FORMATS = ("int4", "mxfp4", "nvfp4")
+GROUP = {"int4": 128, "mxfp4": 32, "nvfp4": 16}
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def lib():
+    """Load liboracle.so, building it with gcc first if it is not there."""
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_e2m1_code.argtypes = [ctypes.c_float]
+        L.oracle_e2m1_code.restype = ctypes.c_int
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_value.restype = ctypes.c_float
+        L.oracle_e4m3_code.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_code.restype = ctypes.c_int
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_value.restype = ctypes.c_float
+        L.oracle_fp16_code.argtypes = [ctypes.c_float]
+        L.oracle_fp16_code.restype = ctypes.c_int
+        L.oracle_fp16_value.argtypes = [ctypes.c_int]
+        L.oracle_fp16_value.restype = ctypes.c_float
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_set_ties_toward_zero.argtypes = [ctypes.c_int]
+        L.oracle_set_ties_toward_zero.restype = None
+        L.oracle_absmax_int_group.argtypes = [_p, _i64, ctypes.c_int, _p]
+        L.oracle_absmax_int_group.restype = ctypes.c_int
+        L.oracle_mx_scale_exponent.argtypes = [ctypes.c_float]
+        L.oracle_mx_scale_exponent.restype = ctypes.c_int
+        L.oracle_nv_block_scale_code.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_nv_block_scale_code.restype = ctypes.c_int
+        L.oracle_nv_global_scale.argtypes = [_p, _i64, _i64, _i64]
+        L.oracle_nv_global_scale.restype = ctypes.c_float
+        L.oracle_quantize_int4.argtypes = [_p, _i64, _i64, _i64, _i64, _p, _p]
+        L.oracle_quantize_int4.restype = ctypes.c_int
+        L.oracle_quantize_mxfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+        L.oracle_quantize_mxfp4.restype = ctypes.c_int
+        L.oracle_quantize_nvfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _p]
+        L.oracle_quantize_nvfp4.restype = ctypes.c_int
+        L.oracle_dequant_int4.argtypes = [_p, _p, _i64, _i64, _i64, _p]
+        L.oracle_dequant_int4.restype = None
+        L.oracle_dequant_mxfp4.argtypes = [_p, _p, _i64, _i64, _p]
+        L.oracle_dequant_mxfp4.restype = None
+        L.oracle_dequant_nvfp4.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p]
+        L.oracle_dequant_nvfp4.restype = None
+        L.oracle_f32_to_bf16_array.argtypes = [_p, _i64, _p]
+        L.oracle_f32_to_bf16_array.restype = None
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(w) -> np.ndarray:
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+    if w.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    return w
+
+
+# --------------------------------------------------------------------------
+# single-value helpers (pins)
+# --------------------------------------------------------------------------
+def e2m1_code(a: float) -> int:
+    return lib().oracle_e2m1_code(a)
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e4m3_code(t: float) -> int:
+    return lib().oracle_e4m3_code(t)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(code)
+
+
+def fp16_code(t: float) -> int:
+    return lib().oracle_fp16_code(t)
+
+
+def fp16_value(code: int) -> float:
+    return lib().oracle_fp16_value(code)
+
+
+def mx_scale_exponent(amax: float) -> int:
+    return lib().oracle_mx_scale_exponent(amax)
+
+
+def nv_block_scale_code(amax_b: float, gs: float) -> int:
+    return lib().oracle_nv_block_scale_code(amax_b, gs)
+
+
+def set_ties_toward_zero(on: bool) -> None:
+    """Test-only switch: exact E2M1/E4M3/FP16/INT ties go to the lower
+    neighbour (the formats.py argmin behaviour) instead of the even code."""
+    lib().oracle_set_ties_toward_zero(1 if on else 0)
+
+
+def absmax_int_group(w, qmax: int):
+    """One symmetric absmax group: (fp16 scale code, integer codes)."""
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float32).ravel())
+    q = np.zeros(w.size, dtype=np.int32)
+    code = lib().oracle_absmax_int_group(_ptr(w), w.size, qmax, _ptr(q))
+    return code, q
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# quantize / dequantize
+# --------------------------------------------------------------------------
+class QTensor:
+    """Oracle-side quantized tensor: packed codes, raw scale bytes, gs."""
+
+    def __init__(self, fmt, rows, cols, codes, scales, gs=None):
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+        self.codes, self.scales, self.gs = codes, scales, gs
+
+
+def quantize(fmt: str, w, gs: float | None = None) -> QTensor:
+    w = _f32(w)
+    rows, cols = w.shape
+    g = GROUP[fmt]
+    if cols % g:
+        raise ValueError(f"cols {cols} is not a multiple of {g}")
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    L = lib()
+    if fmt == "int4":
+        scales = np.zeros((rows, cols // g), dtype=np.uint16)
+        rc = L.oracle_quantize_int4(_ptr(w), rows, cols, cols, g, _ptr(codes), _ptr(scales))
+        out_gs = None
+    elif fmt == "mxfp4":
+        scales = np.zeros((rows, cols // g), dtype=np.uint8)
+        rc = L.oracle_quantize_mxfp4(_ptr(w), rows, cols, cols, _ptr(codes), _ptr(scales))
+        out_gs = None
+    elif fmt == "nvfp4":
+        scales = np.zeros((rows, cols // g), dtype=np.uint8)
+        gs_out = np.zeros(1, dtype=np.float32)
+        gs_in = None if gs is None else np.array([gs], dtype=np.float32)
+        rc = L.oracle_quantize_nvfp4(_ptr(w), rows, cols, cols,
+                                     None if gs_in is None else _ptr(gs_in),
+                                     _ptr(codes), _ptr(scales), _ptr(gs_out))
+        out_gs = float(gs_out[0])
+    else:
+        raise ValueError(fmt)
+    if rc != 0:
+        raise ValueError(f"oracle quantize failed ({rc})")
+    return QTensor(fmt, rows, cols, codes, scales, out_gs)
+
+
+def nv_global_scale(w) -> float:
+    w = _f32(w)
+    return float(lib().oracle_nv_global_scale(_ptr(w), w.shape[0], w.shape[1], w.shape[1]))
+
+
+def dequant(q: QTensor) -> np.ndarray:
+    """fp32 dequantized values: fp32(code value * scale as stored)."""
+    out = np.empty((q.rows, q.cols), dtype=np.float32)
+    codes = np.ascontiguousarray(q.codes)
+    scales = np.ascontiguousarray(q.scales)
+    L = lib()
+    if q.fmt == "int4":
+        L.oracle_dequant_int4(_ptr(codes), _ptr(scales), q.rows, q.cols, 128, _ptr(out))
+    elif q.fmt == "mxfp4":
+        L.oracle_dequant_mxfp4(_ptr(codes), _ptr(scales), q.rows, q.cols, _ptr(out))
+    else:
+        L.oracle_dequant_nvfp4(_ptr(codes), _ptr(scales), q.gs, q.rows, q.cols, _ptr(out))
+    return out
+
+
+def dequant_rows(q: QTensor, rows) -> np.ndarray:
+    """Dequantize a subset of rows (for sampled checks at full size)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    sub = QTensor(q.fmt, len(rows), q.cols, np.ascontiguousarray(q.codes[rows]),
+                  np.ascontiguousarray(q.scales[rows]), q.gs)
+    return dequant(sub)
+
+
+# --------------------------------------------------------------------------
+# matmul references (fp64)
+# --------------------------------------------------------------------------
+def matmul_f64(a, w_deq) -> np.ndarray:
+    """out[m, n] = sum_k a[m, k] * w'[n, k], in fp64."""
+    a64 = np.asarray(a, dtype=np.float64)
+    w64 = np.asarray(w_deq, dtype=np.float64)
+    return a64 @ w64.T
+
+
+def gemv(q: QTensor, x) -> np.ndarray:
+    """W4A16 GEMV: y[b, n] = sum_k x[b, k] * w'[n, k] (fp64)."""
+    return matmul_f64(x, dequant(q))
+
+
+def gemm_w4a16(a, q: QTensor, rows=None) -> np.ndarray:
+    """W4A16 GEMM C = A w'^T (fp64); `rows` selects output rows of C."""
+    a = np.asarray(a, dtype=np.float32)
+    if rows is not None:
+        a = a[np.asarray(rows)]
+    return matmul_f64(a, dequant(q))
+
+
+def gemm_w4a4(a, q: QTensor, rows=None, aq: QTensor | None = None) -> np.ndarray:
+    """W4A4 MXFP4 GEMM: C = deq(mxfp4(A)) deq(W)^T (fp64)."""
+    if q.fmt != "mxfp4":
+        raise ValueError("W4A4 is defined for MXFP4 operands")
+    if aq is None:
+        a = _f32(a)
+        if rows is not None:
+            a = np.ascontiguousarray(a[np.asarray(rows)])
+        aq = quantize("mxfp4", a)
+    elif rows is not None:
+        aq = QTensor("mxfp4", len(rows), aq.cols, aq.codes[np.asarray(rows)],
+                     aq.scales[np.asarray(rows)])
+    return matmul_f64(dequant(aq), dequant(q))
+
+
+def grouped_gemm(a, gather, offsets, q_all: QTensor, n: int, experts=None) -> np.ndarray:
+    """Grouped expert GEMM: for expert e, rows p in [offsets[e], offsets[e+1])
+    get C[p] = a[gather[p]] . w'_e^T, where w'_e is rows [e*n, (e+1)*n) of
+    the expert-major quantized weight.  Returns fp64 [P, n]; rows of experts
+    not listed in `experts` (when given) are left NaN."""
+    a = np.asarray(a, dtype=np.float32)
+    gather = np.asarray(gather)
+    offsets = np.asarray(offsets)
+    E = len(offsets) - 1
+    P = int(offsets[-1])
+    out = np.full((P, n), np.nan, dtype=np.float64)
+    for e in (range(E) if experts is None else experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        w_e = dequant_rows(q_all, np.arange(e * n, (e + 1) * n))
+        out[lo:hi] = matmul_f64(a[gather[lo:hi]], w_e)
+    return out
