@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the 4-bit quantize + W4 matmul path on one MI355X.
+
+Headline workload (one "step"): the MXFP4 decode GEMV y = x W'^T with W
+28672 x 8192 (MXFP4, 124.78 MB of codes + E8M0 scales), for the three
+decode batches B = 1, 4 and 16 -- three launches, each streaming the whole
+weight once.  Inputs are resident in HBM before timing.  Every launch reads
+a different one of several identical weight copies, so no launch finds the
+weights in the 256 MB Infinity Cache left there by the previous one.
+
+value = weight bytes streamed per step / step time  (GB/s, higher is better)
+
+The same JSON line carries:
+  * roofline   -- the dominant GEMV launch: algorithmic bytes per launch
+                  (weights + x + y) over its average duration, measured with
+                  HIP events on the launch stream, against 8 TB/s;
+  * cpu_baseline -- the CPU oracle (plain C quantizer/dequantizer + numpy
+                  fp64 matmul) timed on the same workload on the host cores;
+  * extra      -- the other workloads: weight quantization throughput, the
+                  INT4 g128 GEMV, the NVFP4 W4A16 prefill GEMM, the MoE
+                  grouped expert GEMM and the W4A4 MXFP4 GEMM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 matrix cores
+METRIC = "W4 GEMV weight GB/s and W4 GEMM TFLOP/s vs MI355X roofline, 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=6, help="weight copies rotated across launches")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-extra", action="store_true", help="headline workload only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of extra workloads to run")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class LaunchTimer:
+    """Average duration of repeated launches of one kind, from HIP events
+    recorded on the launch stream around each launch."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def around(self, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+
+
+def timed(torch, fn, iters, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    lt = LaunchTimer(torch)
+    for _ in range(iters):
+        lt.around(fn)
+    torch.cuda.synchronize()
+    return lt.mean_ms()
+
+
+def cpu_cores():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    return min(n, int(omp)) if omp and omp.isdigit() else n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); "
+              "the multi-GPU sharding of the path is described in DESIGN.md, not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w4_gemm_amd as q4
+    from w4_gemm_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    q4.lib()  # fails loudly if the HIP library is missing
+
+    # ---------------------------------------------------------------- headline
+    log("generating the MXFP4 decode workload (28672 x 8192)")
+    wl = workloads.mxfp4_gemv(seed=args.seed)
+    W = wl.tensors["W"].to(dev)
+    N, K = W.shape
+    batches = wl.meta["batches"]
+    xs = {b: wl.tensors[f"x{b}"].to(dev) for b in batches}
+    q0 = q4.quantize(W, "mxfp4")
+    torch.cuda.synchronize()
+    copies = [q0] + [q0.clone() for _ in range(args.copies - 1)]
+    wbytes = q0.codes.numel() + q0.scales.numel()
+    ys = {b: torch.empty((b, N), dtype=torch.bfloat16, device=dev) for b in batches}
+
+    stream = torch.cuda.current_stream()
+    timers = {b: LaunchTimer(torch) for b in batches}
+    counter = [0]
+
+    def step(record):
+        for b in batches:
+            Wc = copies[counter[0] % len(copies)]
+            counter[0] += 1
+            if record:
+                timers[b].around(lambda: q4.q4_gemv(Wc, xs[b], ys[b], stream=stream))
+            else:
+                q4.q4_gemv(Wc, xs[b], ys[b], stream=stream)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step(True)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    value = len(batches) * wbytes / (ms_per_step * 1e-3) / 1e9
+
+    per_b = {}
+    for b in batches:
+        ms = timers[b].mean_ms()
+        alg = wbytes + b * K * 2 + b * N * 2
+        per_b[b] = {"us": ms * 1e3, "weight_GBps": wbytes / (ms * 1e-3) / 1e9,
+                    "alg_GBps": alg / (ms * 1e-3) / 1e9, "alg_bytes": alg}
+    dom = max(batches, key=lambda b: per_b[b]["us"])
+    achieved = per_b[dom]["alg_GBps"]
+    traffic = None
+    prof = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "gemv_mxfp4_28672x8192_traffic.json")
+    if os.path.exists(prof):
+        try:
+            rec = json.load(open(prof))
+            if rec.get("kernel_sha") == _kernel_sha("gemv.hip") and str(dom) in rec.get("bytes_per_launch", {}):
+                traffic = rec["bytes_per_launch"][str(dom)]
+        except Exception:
+            traffic = None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"gemv_kernel<MXFP4> B={dom}", "alg_bytes_per_launch": per_b[dom]["alg_bytes"],
+                "avg_launch_us": round(per_b[dom]["us"], 3)}
+
+    extra = {"decode_gemv_per_batch": {str(b): {k: round(v, 3) for k, v in per_b[b].items()}
+                                       for b in batches},
+             "weight_copies": len(copies)}
+
+    # quantization of the decode weight
+    qt = empty = q4.empty_q4("mxfp4", N, K, device=dev)
+    ms = timed(torch, lambda: q4.q4_quantize(W, empty), 10, 3)
+    qbytes = N * K * 2 + wbytes
+    extra["quantize_mxfp4_28672x8192"] = {"us": round(ms * 1e3, 2),
+                                          "GBps": round(qbytes / (ms * 1e-3) / 1e9, 1),
+                                          "bytes": qbytes}
+    del qt, empty
+    only = set(filter(None, args.only.split(",")))
+
+    def want(name):
+        return not args.no_extra and (not only or name in only)
+
+    if want("int4"):
+        extra["int4_g128_gemv_1024"] = bench_int4(torch, q4, workloads, dev, args.seed)
+    if want("nvfp4"):
+        extra["nvfp4_w4a16_gemm_4096x8192x8192"] = bench_nvfp4(torch, q4, workloads, dev, args.seed)
+    if want("moe"):
+        extra["moe_grouped_mxfp4_64x2048x7168"] = bench_moe(torch, q4, workloads, dev, args.seed)
+    if want("w4a4"):
+        extra["w4a4_mxfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del copies
+        cpu = cpu_baseline(wl, wbytes, batches)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mxfp4_decode_gemv", "N": N, "K": K, "batches": list(batches),
+                   "weight_format": "MXFP4 (E2M1 + E8M0 per 32)", "accumulate": "fp32",
+                   "global_batch": sum(batches), "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_sha(name):
+    import hashlib
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (name, "q4_mma.h", "q4_device.h"):
+        h.update(open(os.path.join(base, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def bench_int4(torch, q4, workloads, dev, seed):
+    wl = workloads.int4_gemv(seed=seed)
+    W = wl.tensors["W"].to(dev)
+    x = wl.tensors["x"].to(dev)
+    q = q4.quantize(W, "int4")
+    y = torch.empty((1, W.shape[0]), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: q4.q4_gemv(q, x, y), 200, 20)
+    qms = timed(torch, lambda: q4.q4_quantize(W, q), 50, 5)
+    return {"gemv_us": round(ms * 1e3, 3), "quantize_us": round(qms * 1e3, 3),
+            "weight_bytes": q.nbytes, "note": "0.53 MB of weights: launch-bound, reported in us"}
+
+
+def bench_nvfp4(torch, q4, workloads, dev, seed):
+    log("generating the NVFP4 prefill workload")
+    wl = workloads.nvfp4_gemm(seed=seed)
+    A = wl.tensors["A"].to(dev)
+    W = wl.tensors["W"].to(dev)
+    M, K = A.shape
+    N = W.shape[0]
+    q = q4.quantize(W, "nvfp4")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: q4.q4_gemm(A, q, C), 10, 2)
+    qms = timed(torch, lambda: q4.q4_quantize(W, q), 10, 2)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "quantize_us": round(qms * 1e3, 1),
+            "quantize_GBps": round((N * K * 2 * 2 + q.nbytes) / (qms * 1e-3) / 1e9, 1)}
+
+
+def bench_moe(torch, q4, workloads, dev, seed):
+    log("generating the MoE workload (64 x 2048 x 7168)")
+    wl = workloads.moe_grouped(seed=seed)
+    W = wl.tensors["W"].to(dev)
+    A = wl.tensors["A"].to(dev)
+    r = wl.meta["routing"]
+    N = wl.meta["N"]
+    q = q4.quantize(W, "mxfp4")
+    del W
+    g = torch.from_numpy(r.gather).to(dev)
+    o = torch.from_numpy(r.offsets).to(dev)
+    P = len(r.gather)
+    C = torch.empty((P, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: q4.q4_grouped_gemm(A, g, o, q, N, C), 20, 3)
+    wbytes = q.codes.numel() + q.scales.numel()
+    flops = 2.0 * P * N * wl.meta["K"]
+    return {"us": round(ms * 1e3, 1), "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2), "routed_rows": P,
+            "rows_per_expert_min_max": [int(min(r.offsets[1:] - r.offsets[:-1])),
+                                        int(max(r.offsets[1:] - r.offsets[:-1]))]}
+
+
+def bench_w4a4(torch, q4, workloads, dev, seed):
+    log("generating the W4A4 workload (8192^3)")
+    wl = workloads.w4a4_gemm(seed=seed)
+    A = wl.tensors["A"].to(dev)
+    W = wl.tensors["W"].to(dev)
+    M, K = A.shape
+    N = W.shape[0]
+    qw = q4.quantize(W, "mxfp4")
+    qa = q4.quantize(A, "mxfp4")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: q4.q4_gemm(qa, qw, C), 10, 2)
+    ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+            "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+            "act_quantize_us": round(ams * 1e3, 1),
+            "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline(wl, wbytes, batches):
+    """The oracle, as it stands, on the headline workload: for each batch it
+    dequantizes the MXFP4 weight (plain C) and takes the fp64 product
+    (numpy).  Repeated until about 10 s of CPU work."""
+    import numpy as np
+
+    import oracle
+
+    log("cpu baseline: oracle quantize (setup)")
+    w = wl.tensors["W"].float().numpy()
+    qr = oracle.quantize("mxfp4", w)
+    del w
+    xs = {b: wl.tensors[f"x{b}"].float().numpy() for b in batches}
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        for b in batches:
+            oracle.gemv(qr, xs[b])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or steps >= 5:
+            break
+    per_step = el / steps
+    return {"value": round(len(batches) * wbytes / per_step / 1e9, 3), "unit": "GB/s",
+            "cores": cpu_cores(), "kind": "oracle",
+            "sample": f"full workload: 28672x8192 MXFP4 weight, B={list(batches)}, {steps} step(s), "
+                      f"{per_step:.2f} s/step"}
+
+
+if __name__ == "__main__":
+    main()

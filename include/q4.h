@@ -1,0 +1,168 @@
+/*
+ * q4.h -- C ABI of libq4.so: 4-bit absmax block quantization of bf16
+ * weights (INT4 g128, MXFP4, NVFP4) and the W4 matmuls that consume them,
+ * as hand-written HIP kernels for AMD gfx950 (MI355X).
+ *
+ * Formats (one row of K values is split into blocks of g along K):
+ *   Q4_INT4_G128  codes -8..7 (4-bit two's complement), one fp16 scale per
+ *                 128 values, scale = fp16(amax/7), code = clamp(rne(w/s)).
+ *                 ("Quantization in deployment", format cheat sheet, W4A16
+ *                 row; "Low-bit inference for very large MoE", fake_int4;
+ *                 "Quantization chains", bits per weight: 4.125.)
+ *   Q4_MXFP4      E2M1 codes (grid +-{0,0.5,1,1.5,2,3,4,6}), one E8M0
+ *                 power-of-two scale per 32 values,
+ *                 scale = 2^(floor(log2(max(amax,1e-12))) - 2).
+ *                 ("Quantization in deployment", formats.py mxfp4(); 4.25 bits.)
+ *   Q4_NVFP4      E2M1 codes, one E4M3 scale per 16 values plus one fp32
+ *                 tensor scale gs = max(amax_tensor,1e-12)/2688;
+ *                 block scale = E4M3(min(amax_b/6/gs, 448)), element
+ *                 divided by E4M3(scale)*gs.  ("Quantization in deployment",
+ *                 formats.py nvfp4(); "Quantization chains", NVFP4 vs MXFP4.)
+ * Every rounding is to nearest, ties to the even code; E2M1 keeps the sign
+ * bit of the input; a block whose stored scale is 0 has magnitude codes 0.
+ *
+ * Layout of a quantized tensor (q4_tensor), all device memory owned by the
+ * caller, row-major and dense:
+ *   codes   uint8 [rows][cols/2]; element k of a row sits in byte k/2,
+ *           even k in bits 3:0, odd k in bits 7:4.  16-byte aligned.
+ *   scales  INT4: fp16 bits [rows][cols/128]; MXFP4: biased E8M0 exponent
+ *           [rows][cols/32]; NVFP4: E4M3 bits [rows][cols/16].  4-byte aligned.
+ *   global_scale  NVFP4 only: device fp32[1], the multiplier gs; else NULL.
+ *
+ * Conventions for every call:
+ *   - Pointers named *_bf16 are device bf16 arrays; leading dimensions (ld*)
+ *     are in elements, >= the row length, multiples of 8, and the base
+ *     pointers 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device work
+ *     is enqueued on it; the call returns after the launch, not after the
+ *     work.  The library never allocates, frees or synchronizes.
+ *   - Arguments are validated on the host before any HIP call; a bad
+ *     argument returns its error code and launches nothing.  A failed launch
+ *     returns Q4_ERR_HIP; q4_last_hip_error() gives the hipError_t of the
+ *     calling thread's last failure.
+ *   - Inputs must be finite.  Calls on distinct outputs may run
+ *     concurrently; outputs must not alias inputs.
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum q4_format {
+    Q4_INT4_G128 = 0,
+    Q4_MXFP4 = 1,
+    Q4_NVFP4 = 2
+} q4_format;
+
+typedef enum q4_status {
+    Q4_OK = 0,
+    Q4_ERR_NULL = -1,   /* a required pointer is NULL                      */
+    Q4_ERR_SHAPE = -2,  /* a size is negative, too large or not a multiple */
+    Q4_ERR_ALIGN = -3,  /* a pointer or leading dimension is misaligned    */
+    Q4_ERR_FORMAT = -4, /* unknown format, or a format the call rejects    */
+    Q4_ERR_HIP = -6     /* the HIP launch failed; see q4_last_hip_error()  */
+} q4_status;
+
+typedef struct q4_tensor {
+    int32_t fmt;          /* q4_format                                     */
+    int32_t reserved;     /* must be 0                                     */
+    int64_t rows;         /* N for weights, M for activations              */
+    int64_t cols;         /* K, a multiple of the format's block size      */
+    void* codes;          /* uint8 [rows][cols/2]                          */
+    void* scales;         /* [rows][cols/g], see above                     */
+    float* global_scale;  /* NVFP4: fp32[1]; other formats: NULL           */
+} q4_tensor;
+
+/* Library version (major*100 + minor). */
+int q4_version(void);
+
+/* Static text for a q4_status value. */
+const char* q4_status_string(int status);
+
+/* hipError_t of the calling thread's last Q4_ERR_HIP (0 if none). */
+int q4_last_hip_error(void);
+
+/*
+ * Bytes of codes and scales for a rows x cols tensor of format fmt
+ * ("Quantization chains", bits per weight: codes are 4 bits, scales 16/128,
+ * 8/32 and 8/16 bits per value).  Either output pointer may be NULL.
+ * Q4_ERR_SHAPE if rows < 0, cols < 0 or cols is not a multiple of the block.
+ */
+q4_status q4_sizes(int fmt, int64_t rows, int64_t cols, size_t* codes_bytes,
+                   size_t* scales_bytes);
+
+/*
+ * Quantize a bf16 matrix src [dst->rows][ld] (first dst->cols columns) into
+ * dst, by round-to-nearest absmax block quantization along each row
+ * ("LLM quantization", the absmax method: the group's largest magnitude
+ * sets the scale, every value is divided by it and rounded).
+ * NVFP4: if nv_global_in (device fp32[1]) is not NULL its value is used as
+ * gs; otherwise gs is computed from the whole matrix (one extra read pass)
+ * and written to dst->global_scale.  nv_global_in must be NULL for the other
+ * formats.  rows == 0 or cols == 0 is a no-op (for NVFP4 without
+ * nv_global_in, gs is still written: max(0,1e-12)/2688).
+ */
+q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
+                      const float* nv_global_in, void* stream);
+
+/*
+ * Dequantize src into dst [src->rows][ld]: value = fp32(code * scale) with
+ * the scale as stored (NVFP4: scale = fp32(E4M3 * gs)).  dst_dtype 0 writes
+ * bf16 (the fp32 value rounded to nearest even), 1 writes fp32 (ld a
+ * multiple of 4 for fp32).  This is the multiply-back step of
+ * "LLM quantization"'s worked example ("divide, round, multiply back").
+ */
+q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld, void* stream);
+
+/*
+ * W4A16 GEMV for decode: y[b][n] = sum_k x[b][k] * w'[n][k] for b < B,
+ * n < W->rows, w' the dequantized weight; fp32 accumulation, bf16 output
+ * ("Low-bit inference for very large MoE", table "Kernels on different
+ * hardware", row W4A16: weights dequantized in registers, 16-bit compute).
+ * x_bf16 [B][ldx], y_bf16 [B][ldy].  1 <= B <= 16; K = W->cols must be a
+ * multiple of 128.  B == 0 or W->rows == 0 is a no-op.
+ */
+q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx,
+                  void* y_bf16, int64_t ldy, void* stream);
+
+/*
+ * GEMM C[m][n] = sum_k a'[m][k] * w'[n][k], fp32 accumulation, bf16 output
+ * C_bf16 [M][ldc].  Exactly one of A_bf16 / A_q is given:
+ *   A_bf16 [M][lda]  -> W4A16: W of any format dequantized to bf16 feeding
+ *                       bf16 matrix cores (same table, row W4A16);
+ *   A_q (MXFP4, rows M, cols K) with W MXFP4 -> W4A4: both operands enter
+ *                       the block-scaled FP4 matrix cores directly (same
+ *                       table, row W4A4).  Other formats: Q4_ERR_FORMAT.
+ * K = W->cols must be a multiple of 128.  M == 0 or N == 0 is a no-op.
+ */
+q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A_q,
+                  const q4_tensor* W, void* C_bf16, int64_t ldc, void* stream);
+
+/*
+ * Grouped per-expert GEMM for MoE ("Low-bit inference for very large MoE",
+ * "A few details": one low-bit weight matrix per expert, rows grouped by
+ * routing).  W holds E experts stacked expert-major: W->rows == E*N, expert
+ * e owns rows [e*N, (e+1)*N).  For every expert e and every routed row p in
+ * [expert_offsets[e], expert_offsets[e+1]):
+ *     C[p][n] = sum_k A[gather[p]][k] * w'[e*N + n][k]
+ * A_bf16 [T][lda] (T tokens), gather int32 [P] (device), expert_offsets
+ * int32 [E+1] (device, non-decreasing, offsets[0] = 0, offsets[E] = P),
+ * C_bf16 [P][ldc].  The kernels read the offsets on the device (no host
+ * sync) and clamp every range to [0, P]; a row whose gather index is outside
+ * [0, T) is written as zeros.  K = W->cols must be a multiple of 128.
+ */
+q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int32_t* gather,
+                          const int32_t* expert_offsets, int32_t E, int64_t P,
+                          const q4_tensor* W, int64_t N, void* C_bf16, int64_t ldc,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

@@ -1,0 +1,152 @@
+"""The C ABI of libq4.so on the host: it loads without a GPU, exports every
+function include/q4.h declares, and rejects bad arguments with the right
+status before any HIP call (no call here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4_gemm_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+OK, NULL, SHAPE, ALIGN, FMT = 0, -1, -2, -3, -4
+
+# Fake device addresses: never dereferenced, since every call below fails
+# validation (or is a no-op) before reaching a kernel.
+A16 = 0x7F0000000000
+A_ODD = A16 + 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(q4_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_grouped_gemm"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = q4.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert q4.q4_version() >= 100
+
+
+def test_status_strings():
+    L = q4.lib()
+    for st in (0, -1, -2, -3, -4, -6):
+        assert L.q4_status_string(st)
+    assert L.q4_status_string(12345) == b"unknown status"
+    assert L.q4_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("fmt,cols,codes,scales", [
+    (q4.INT4_G128, 1024, 512, 16), (q4.MXFP4, 1024, 512, 32), (q4.NVFP4, 1024, 512, 64),
+])
+def test_sizes(fmt, cols, codes, scales):
+    assert q4.q4_sizes(fmt, 1, cols) == (codes, scales)
+    assert q4.q4_sizes(fmt, 28672, 8192)[0] == 28672 * 4096
+    assert q4.q4_sizes(fmt, 0, cols) == (0, 0)
+
+
+def test_sizes_rejects():
+    L = q4.lib()
+    assert L.q4_sizes(7, 1, 128, None, None) == FMT
+    assert L.q4_sizes(q4.MXFP4, 1, 48, None, None) == SHAPE
+    assert L.q4_sizes(q4.INT4_G128, 1, 64, None, None) == SHAPE
+    assert L.q4_sizes(q4.MXFP4, -1, 64, None, None) == SHAPE
+
+
+def desc(fmt=q4.MXFP4, rows=64, cols=256, codes=A16, scales=A16, gs=None, reserved=0):
+    return q4._Q4TensorC(fmt, reserved, rows, cols, codes, scales, gs)
+
+
+def call_quantize(src, ld, d, gs_in=None):
+    return q4.lib().q4_quantize(src, ld, ctypes.byref(d), gs_in, None)
+
+
+def test_quantize_validation():
+    L = q4.lib()
+    assert L.q4_quantize(A16, 256, None, None, None) == NULL
+    assert call_quantize(None, 256, desc()) == NULL
+    assert call_quantize(A16, 256, desc(fmt=9)) == FMT
+    assert call_quantize(A16, 256, desc(reserved=1)) == FMT
+    assert call_quantize(A16, 256, desc(cols=48)) == SHAPE
+    assert call_quantize(A16, 256, desc(rows=-1)) == SHAPE
+    assert call_quantize(A16, 128, desc()) == SHAPE              # ld < cols
+    assert call_quantize(A16, 260, desc()) == ALIGN              # ld not a multiple of 8
+    assert call_quantize(A_ODD, 256, desc()) == ALIGN
+    assert call_quantize(A16, 256, desc(codes=A16 + 4)) == ALIGN
+    assert call_quantize(A16, 256, desc(codes=None)) == NULL
+    assert call_quantize(A16, 256, desc(fmt=q4.NVFP4)) == NULL   # NVFP4 needs global_scale
+    assert call_quantize(A16, 256, desc(gs=A16)) == FMT          # only NVFP4 takes one
+    assert call_quantize(A16, 256, desc(), gs_in=A16) == FMT
+    assert call_quantize(A16, 256, desc(rows=0)) == OK           # empty: no launch
+
+
+def test_dequant_validation():
+    L = q4.lib()
+    d = desc()
+    assert L.q4_dequant(ctypes.byref(d), A16, 2, 256, None) == FMT
+    assert L.q4_dequant(ctypes.byref(d), None, 0, 256, None) == NULL
+    assert L.q4_dequant(ctypes.byref(d), A16, 0, 100, None) == SHAPE
+    assert L.q4_dequant(ctypes.byref(d), A16, 1, 258, None) == ALIGN
+    assert L.q4_dequant(ctypes.byref(desc(rows=0)), None, 0, 256, None) == OK
+
+
+def test_gemv_validation():
+    L = q4.lib()
+    d = desc(rows=1024, cols=1024)
+    assert L.q4_gemv(ctypes.byref(d), A16, 17, 1024, A16, 1024, None) == SHAPE
+    assert L.q4_gemv(ctypes.byref(d), A16, -1, 1024, A16, 1024, None) == SHAPE
+    assert L.q4_gemv(ctypes.byref(desc(rows=8, cols=96)), A16, 1, 96, A16, 8, None) == SHAPE
+    assert L.q4_gemv(ctypes.byref(d), None, 1, 1024, A16, 1024, None) == NULL
+    assert L.q4_gemv(ctypes.byref(d), A16, 1, 1024, None, 1024, None) == NULL
+    assert L.q4_gemv(ctypes.byref(d), A16, 2, 1000, A16, 1024, None) == SHAPE
+    assert L.q4_gemv(ctypes.byref(d), A16, 2, 1024, A16, 1000, None) == SHAPE
+    assert L.q4_gemv(ctypes.byref(d), A_ODD, 1, 1024, A16, 1024, None) == ALIGN
+    assert L.q4_gemv(ctypes.byref(d), A16, 0, 1024, A16, 1024, None) == OK
+
+
+def test_gemm_validation():
+    L = q4.lib()
+    w = desc(rows=512, cols=512)
+    a = desc(rows=64, cols=512)
+    nv = desc(fmt=q4.NVFP4, rows=64, cols=512, gs=A16)
+    assert L.q4_gemm(64, A16, 512, ctypes.byref(a), ctypes.byref(w), A16, 512, None) == FMT
+    assert L.q4_gemm(64, None, 512, None, ctypes.byref(w), A16, 512, None) == NULL
+    assert L.q4_gemm(64, None, 0, ctypes.byref(nv), ctypes.byref(w), A16, 512, None) == FMT
+    assert L.q4_gemm(32, None, 0, ctypes.byref(a), ctypes.byref(w), A16, 512, None) == SHAPE
+    assert L.q4_gemm(64, A16, 512, None, ctypes.byref(desc(rows=512, cols=96)), A16, 512,
+                     None) == SHAPE
+    assert L.q4_gemm(64, A16, 500, None, ctypes.byref(w), A16, 512, None) == SHAPE
+    assert L.q4_gemm(64, A16, 512, None, ctypes.byref(w), A16, 500, None) == SHAPE
+    assert L.q4_gemm(-1, A16, 512, None, ctypes.byref(w), A16, 512, None) == SHAPE
+    assert L.q4_gemm(0, A16, 512, None, ctypes.byref(w), A16, 512, None) == OK
+
+
+def test_grouped_validation():
+    L = q4.lib()
+    w = desc(rows=8 * 128, cols=512)
+    ok_args = dict(A=A16, lda=512, T=16, gather=A16, off=A16, E=8, P=32, N=128, C=A16, ldc=128)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return L.q4_grouped_gemm(a["A"], a["lda"], a["T"], a["gather"], a["off"], a["E"], a["P"],
+                                 ctypes.byref(kw.get("W", w)), a["N"], a["C"], a["ldc"], None)
+
+    assert call(N=100) == SHAPE                  # W rows != E*N
+    assert call(E=-1) == SHAPE
+    assert call(gather=None) == NULL
+    assert call(off=None) == NULL
+    assert call(gather=A16 + 2) == ALIGN
+    assert call(lda=500) == SHAPE
+    assert call(ldc=100) == SHAPE
+    assert call(P=0) == OK
+    assert call(W=desc(rows=8 * 128, cols=96), N=128) == SHAPE

@@ -1,0 +1,197 @@
+"""GPU parity of q4_quantize / q4_dequant against the oracle: packed codes,
+scales and the NVFP4 global scale bit for bit; dequantized values bit for
+bit (fp32 and bf16)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4_gemm_amd as q4
+from w4_gemm_amd import workloads
+from q4_helpers import assert_quant_equal, log, to_f32
+
+pytestmark = pytest.mark.gpu
+FMTS = ("int4", "mxfp4", "nvfp4")
+DEV = "cuda:0"
+
+
+def quant_both(w_bf16: torch.Tensor, fmt: str, gs=None):
+    wd = w_bf16.to(DEV)
+    gs_t = None if gs is None else torch.tensor([gs], dtype=torch.float32, device=DEV)
+    qg = q4.quantize(wd, fmt, nv_global_in=gs_t)
+    torch.cuda.synchronize()
+    qr = oracle.quantize(fmt, to_f32(w_bf16), gs=gs)
+    return qg, qr
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 128), (3, 256), (37, 640), (130, 1024), (257, 384)])
+def test_quantize_small_random(fmt, shape):
+    log("quantize", fmt, shape)
+    rows, cols = shape
+    w = workloads.matrix(f"tq/{rows}x{cols}", rows, cols, 0.02, seed=11,
+                         outlier_frac=0.002, outlier_mult=25.0)
+    qg, qr = quant_both(w, fmt)
+    assert_quant_equal(qg, qr, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_all_bf16_values(fmt):
+    """Every finite bf16 bit pattern, grouped into blocks in three different
+    orders so each value meets many block scales."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    v = v[np.isfinite(v)]
+    if fmt == "int4":
+        v = v[np.abs(v) < 4e5]  # fp16 scale range (|w| < 7*65504)
+    rng = np.random.default_rng(12)
+    for order in ("sorted", "shuffled", "mixed"):
+        x = v.copy()
+        if order == "shuffled":
+            rng.shuffle(x)
+        elif order == "mixed":  # small values next to a large one in each block
+            x = np.sort(np.abs(x))[::-1].copy() * np.where(rng.random(x.size) < 0.5, -1, 1)
+            x = x[: (x.size // 16) * 16].reshape(-1, 16)[:, ::-1].reshape(-1).copy()
+        n = (x.size // 1024) * 1024
+        w = torch.from_numpy(x[:n].reshape(-1, 1024)).to(torch.bfloat16)
+        log("all bf16", fmt, order, tuple(w.shape))
+        qg, qr = quant_both(w, fmt)
+        assert_quant_equal(qg, qr, fmt)
+
+
+@pytest.mark.parametrize("fmt", ("mxfp4", "nvfp4"))
+def test_quantize_exact_ties(fmt):
+    """Values that land exactly on E2M1 midpoints (0.25, 0.75, ... 5) after
+    the division: ties go to the even code on both sides."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    rows = []
+    for e in range(-6, 6):
+        blk = np.zeros(32, np.float32)
+        blk[0] = 6.0 * 2.0 ** e           # absmax -> scale 2^(e)  (floor(log2 6) - 2 = 0)
+        blk[1:8] = mids * 2.0 ** e
+        blk[8:15] = -mids * 2.0 ** e
+        rows.append(blk)
+    w = torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+    if fmt == "nvfp4":
+        qg, qr = quant_both(w, fmt, gs=1.0)
+    else:
+        qg, qr = quant_both(w, fmt)
+    assert_quant_equal(qg, qr, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_edge_blocks(fmt):
+    w = np.zeros((8, 256), np.float32)
+    w[1] = -0.0
+    w[2, :] = 1e-30                      # below the 1e-12 clamp
+    w[3, ::2] = 3.0e38                   # near the top of fp32 (MX, NV only)
+    w[4, :] = np.float32(2.0 ** -130)    # bf16 subnormal
+    w[5, 7] = 1.0                        # one nonzero per block
+    w[6, :] = np.linspace(-1, 1, 256)
+    w[7, :] = 448.0 * 6 * np.sign(np.linspace(-1, 1, 256))
+    if fmt == "int4":
+        w[3] = 0.0
+        w[7] = np.sign(w[7]) * 1000.0
+    wt = torch.from_numpy(w).to(torch.bfloat16)
+    qg, qr = quant_both(wt, fmt)
+    assert_quant_equal(qg, qr, fmt)
+
+
+def test_nvfp4_caller_global_scale_and_underflow():
+    w = workloads.matrix("tq/nv", 64, 512, 0.02, seed=13)
+    for gs in (1.0, 0.001, 1e-6, 3.0):
+        qg, qr = quant_both(w, "nvfp4", gs=gs)
+        assert_quant_equal(qg, qr, "nvfp4")
+    # a tiny block next to a large tensor max: its E4M3 scale underflows to 0
+    x = np.zeros((2, 32), np.float32)
+    x[0, 0] = 100.0
+    x[1, :16] = 1e-6
+    x[1, 16:] = -1e-6
+    qg, qr = quant_both(torch.from_numpy(x).to(torch.bfloat16), "nvfp4")
+    assert_quant_equal(qg, qr, "nvfp4")
+    assert np.all(qr.scales[1] == 0)
+
+
+def test_quantize_strided_source_and_empty():
+    base = workloads.matrix("tq/strided", 40, 1024, 0.05, seed=14)
+    view = base[:, :512]                          # ld = 1024 > cols
+    for fmt in FMTS:
+        qg = q4.quantize(base.to(DEV)[:, :512], fmt)
+        torch.cuda.synchronize()
+        qr = oracle.quantize(fmt, to_f32(view))
+        assert_quant_equal(qg, qr, fmt)
+    e = q4.empty_q4("nvfp4", 0, 128, device=DEV)
+    q4.q4_quantize(torch.empty((0, 128), dtype=torch.bfloat16, device=DEV), e)
+    torch.cuda.synchronize()
+    assert e.global_scale.item() == np.float32(1e-12) / np.float32(2688.0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_bit_exact(fmt):
+    w = workloads.matrix("tq/dq", 96, 768, 0.03, seed=15, outlier_frac=0.01, outlier_mult=30.0)
+    qg, qr = quant_both(w, fmt)
+    ref = oracle.dequant(qr)
+    out32 = torch.full((96, 776), float("nan"), device=DEV)
+    q4.q4_dequant(qg, out32[:, :768])
+    out16 = torch.empty((96, 768), dtype=torch.bfloat16, device=DEV)
+    q4.q4_dequant(qg, out16)
+    torch.cuda.synchronize()
+    o32 = out32.cpu().numpy()
+    assert np.array_equal(o32[:, :768].view(np.uint32), ref.view(np.uint32))
+    assert np.all(np.isnan(o32[:, 768:]))         # nothing written past cols
+    o16 = out16.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o16, oracle.f32_to_bf16_bits(ref))
+
+
+def test_quantize_deterministic():
+    w = workloads.matrix("tq/det", 512, 2048, 0.02, seed=16).to(DEV)
+    for fmt in FMTS:
+        a, b = q4.quantize(w, fmt), q4.quantize(w, fmt)
+        torch.cuda.synchronize()
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark uses
+# --------------------------------------------------------------------------
+def test_full_int4_gemv_weight():
+    wl = workloads.int4_gemv()
+    qg, qr = quant_both(wl.tensors["W"], "int4")
+    assert_quant_equal(qg, qr, "int4")
+
+
+def test_full_mxfp4_decode_weight():
+    wl = workloads.mxfp4_gemv(batches=(1,))
+    log("quantize 28672x8192 MXFP4")
+    qg, qr = quant_both(wl.tensors["W"], "mxfp4")
+    assert_quant_equal(qg, qr, "mxfp4")
+
+
+def test_full_nvfp4_prefill_weight():
+    wl = workloads.nvfp4_gemm()
+    log("quantize 8192x8192 NVFP4")
+    qg, qr = quant_both(wl.tensors["W"], "nvfp4")
+    assert_quant_equal(qg, qr, "nvfp4")
+
+
+def test_full_w4a4_operands():
+    wl = workloads.w4a4_gemm()
+    for name in ("A", "W"):
+        log("quantize 8192x8192 MXFP4", name)
+        qg, qr = quant_both(wl.tensors[name], "mxfp4")
+        assert_quant_equal(qg, qr, "mxfp4")
+
+
+def test_full_moe_experts_weight():
+    """All 64 experts quantized in one call on the GPU; the oracle checks
+    four of them completely."""
+    wl = workloads.moe_grouped()
+    W = wl.tensors["W"]
+    N = wl.meta["N"]
+    log("quantize 64x2048x7168 MXFP4")
+    qg = q4.quantize(W.to(DEV), "mxfp4")
+    torch.cuda.synchronize()
+    for e in (0, 21, 42, 63):
+        rows = np.arange(e * N, (e + 1) * N)
+        qr = oracle.quantize("mxfp4", to_f32(W[e * N:(e + 1) * N]))
+        assert_quant_equal(qg, qr, "mxfp4", rows=rows)

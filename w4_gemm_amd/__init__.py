@@ -1,0 +1,240 @@
+"""w4_gemm_amd -- 4-bit absmax block quantization (INT4 g128, MXFP4, NVFP4)
+and the W4 matmuls that consume it, as hand-written HIP kernels for gfx950.
+
+This module is the thin Python binding of libq4.so's C ABI (include/q4.h):
+the functions have the same names and only marshal arguments -- torch
+tensors supply device memory and the current HIP stream, every step of the
+computation runs in the library's kernels.  There is no CPU fallback: if the
+library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "INT4_G128", "MXFP4", "NVFP4", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
+    "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
+    "q4_grouped_gemm", "empty_q4", "quantize", "LIB_PATH",
+]
+
+INT4_G128, MXFP4, NVFP4 = 0, 1, 2
+FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4}
+GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4.so")
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = _lib_handle().q4_status_string(status).decode() if _LIB else str(status)
+        extra = ""
+        if status == -6 and _LIB:
+            extra = f" (hipError {_LIB.q4_last_hip_error()})"
+        super().__init__(f"{call}: status {status}: {msg}{extra}")
+        self.status = status
+
+
+class _Q4TensorC(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("global_scale", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+def _lib_handle():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            from . import _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+        P = ctypes.POINTER(_Q4TensorC)
+        sig = {
+            "q4_version": ([], ctypes.c_int),
+            "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "q4_last_hip_error": ([], ctypes.c_int),
+            "q4_sizes": ([ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_size_t),
+                          ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+            "q4_quantize": ([vp, i64, P, vp, vp], ctypes.c_int),
+            "q4_dequant": ([P, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+            "q4_gemv": ([P, vp, i64, i64, vp, i64, vp], ctypes.c_int),
+            "q4_gemm": ([i64, vp, i64, P, P, vp, i64, vp], ctypes.c_int),
+            "q4_grouped_gemm": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
+                                ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _LIB = L
+    return _LIB
+
+
+def lib():
+    """The loaded libq4.so (built in-tree first if it is missing)."""
+    return _lib_handle()
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise Q4Error(status, call)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _fmt(fmt) -> int:
+    return FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+@dataclass
+class Q4Tensor:
+    """A quantized matrix: rows x cols values, blocks along cols.
+
+    codes  uint8 [rows, cols/2]   (even k in the low nibble)
+    scales INT4: int16 (fp16 bits) [rows, cols/128]; MXFP4: uint8 (E8M0)
+           [rows, cols/32]; NVFP4: uint8 (E4M3) [rows, cols/16]
+    global_scale  NVFP4: float32 [1] (dequant multiplier); else None
+    """
+    fmt: int
+    rows: int
+    cols: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    global_scale: Optional[torch.Tensor] = None
+
+    def c(self) -> _Q4TensorC:
+        return _Q4TensorC(self.fmt, 0, self.rows, self.cols,
+                          self.codes.data_ptr() if self.codes.numel() else None,
+                          self.scales.data_ptr() if self.scales.numel() else None,
+                          None if self.global_scale is None else self.global_scale.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        n = self.codes.numel() + self.scales.numel() * self.scales.element_size()
+        return n + (4 if self.global_scale is not None else 0)
+
+    def clone(self) -> "Q4Tensor":
+        return Q4Tensor(self.fmt, self.rows, self.cols, self.codes.clone(), self.scales.clone(),
+                        None if self.global_scale is None else self.global_scale.clone())
+
+
+def q4_version() -> int:
+    return lib().q4_version()
+
+
+def q4_sizes(fmt, rows: int, cols: int):
+    """(codes bytes, scales bytes) of a rows x cols tensor."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().q4_sizes(_fmt(fmt), rows, cols, ctypes.byref(cb), ctypes.byref(sb)), "q4_sizes")
+    return cb.value, sb.value
+
+
+def empty_q4(fmt, rows: int, cols: int, device="cuda") -> Q4Tensor:
+    """Allocate (with torch) the buffers of a quantized tensor."""
+    f = _fmt(fmt)
+    cb, sb = q4_sizes(f, rows, cols)
+    codes = torch.empty(cb, dtype=torch.uint8, device=device).view(rows, cols // 2) \
+        if rows and cols else torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+    g = GROUP[f]
+    if f == INT4_G128:
+        scales = torch.empty((rows, cols // g), dtype=torch.int16, device=device)
+    else:
+        scales = torch.empty((rows, cols // g), dtype=torch.uint8, device=device)
+    gs = torch.empty(1, dtype=torch.float32, device=device) if f == NVFP4 else None
+    return Q4Tensor(f, rows, cols, codes, scales, gs)
+
+
+def q4_quantize(src: torch.Tensor, dst: Q4Tensor, nv_global_in: Optional[torch.Tensor] = None,
+                stream=None) -> Q4Tensor:
+    """Quantize bf16 src [rows, >= cols] (row stride src.stride(0)) into dst."""
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be a 2-D bf16 tensor with unit column stride")
+    desc = dst.c()
+    _check(lib().q4_quantize(_ptr(src), src.stride(0), ctypes.byref(desc), _ptr(nv_global_in),
+                             _stream(stream)), "q4_quantize")
+    return dst
+
+
+def quantize(src: torch.Tensor, fmt, nv_global_in: Optional[torch.Tensor] = None,
+             stream=None) -> Q4Tensor:
+    """Allocate a Q4Tensor on src's device and quantize src into it."""
+    dst = empty_q4(fmt, src.shape[0], src.shape[1], device=src.device)
+    return q4_quantize(src, dst, nv_global_in, stream)
+
+
+def q4_dequant(src: Q4Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """Dequantize into dst (bf16 or float32, [rows, >= cols])."""
+    if dst.dtype == torch.bfloat16:
+        dt = 0
+    elif dst.dtype == torch.float32:
+        dt = 1
+    else:
+        raise ValueError("dst must be bf16 or float32")
+    if dst.dim() != 2 or dst.stride(1) != 1:
+        raise ValueError("dst must be 2-D with unit column stride")
+    desc = src.c()
+    _check(lib().q4_dequant(ctypes.byref(desc), _ptr(dst), dt, dst.stride(0), _stream(stream)),
+           "q4_dequant")
+    return dst
+
+
+def q4_gemv(W: Q4Tensor, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y[b, n] = sum_k x[b, k] w'[n, k] for b < x.shape[0] (<= 16)."""
+    desc = W.c()
+    _check(lib().q4_gemv(ctypes.byref(desc), _ptr(x), x.shape[0], x.stride(0), _ptr(y),
+                         y.stride(0), _stream(stream)), "q4_gemv")
+    return y
+
+
+def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
+    """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16) or an MXFP4 Q4Tensor
+    (W4A4, with W MXFP4)."""
+    wd = W.c()
+    if isinstance(A, Q4Tensor):
+        ad = A.c()
+        st = lib().q4_gemm(A.rows, None, 0, ctypes.byref(ad), ctypes.byref(wd), _ptr(C),
+                           C.stride(0), _stream(stream))
+    else:
+        st = lib().q4_gemm(A.shape[0], _ptr(A), A.stride(0), None, ctypes.byref(wd), _ptr(C),
+                           C.stride(0), _stream(stream))
+    _check(st, "q4_gemm")
+    return C
+
+
+def q4_grouped_gemm(A: torch.Tensor, gather: torch.Tensor, offsets: torch.Tensor, W: Q4Tensor,
+                    N: int, C: torch.Tensor, stream=None) -> torch.Tensor:
+    """For expert e, rows p in [offsets[e], offsets[e+1]):
+    C[p] = A[gather[p]] . w'_e^T, with W stacked expert-major (E*N rows)."""
+    if gather.dtype != torch.int32 or offsets.dtype != torch.int32:
+        raise ValueError("gather and offsets must be int32")
+    E = offsets.numel() - 1
+    wd = W.c()
+    _check(lib().q4_grouped_gemm(_ptr(A), A.stride(0), A.shape[0], _ptr(gather), _ptr(offsets),
+                                 E, gather.numel(), ctypes.byref(wd), N, _ptr(C), C.stride(0),
+                                 _stream(stream)), "q4_grouped_gemm")
+    return C

@@ -1,0 +1,213 @@
+// api.hip -- the C ABI of libq4.so (declared in include/q4.h): argument
+// validation on the host, then one launcher per call.  No call allocates,
+// frees or synchronizes; every error is returned before any HIP call.
+#include "../../include/q4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "q4_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernels index rows/cols in int
+
+int block_of(int fmt) {
+  switch (fmt) {
+    case Q4_INT4_G128: return 128;
+    case Q4_MXFP4: return 32;
+    case Q4_NVFP4: return 16;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+q4_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return Q4_OK;
+  g_last_hip_error = (int)e;
+  return Q4_ERR_HIP;
+}
+
+// Validates a quantized tensor descriptor.  With `need_data` the codes,
+// scales (and NVFP4 global scale) must be present.
+q4_status check_tensor(const q4_tensor* t) {
+  if (!t) return Q4_ERR_NULL;
+  const int g = block_of(t->fmt);
+  if (!g || t->reserved != 0) return Q4_ERR_FORMAT;
+  if (t->rows < 0 || t->cols < 0 || t->rows >= kMaxDim || t->cols >= kMaxDim) return Q4_ERR_SHAPE;
+  if (t->cols % g) return Q4_ERR_SHAPE;
+  if (t->fmt == Q4_NVFP4) {
+    if (!t->global_scale) return Q4_ERR_NULL;
+    if (!aligned(t->global_scale, 4)) return Q4_ERR_ALIGN;
+  } else if (t->global_scale) {
+    return Q4_ERR_FORMAT;
+  }
+  if (t->rows > 0 && t->cols > 0) {
+    if (!t->codes || !t->scales) return Q4_ERR_NULL;
+    if (!aligned(t->codes, 16) || !aligned(t->scales, 4)) return Q4_ERR_ALIGN;
+  }
+  return Q4_OK;
+}
+
+// A bf16 matrix argument: rows x cols with leading dimension ld.
+q4_status check_bf16(const void* p, int64_t rows, int64_t cols, int64_t ld) {
+  if (rows < 0 || cols < 0) return Q4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return Q4_OK;
+  if (!p) return Q4_ERR_NULL;
+  if (ld < cols) return Q4_ERR_SHAPE;
+  if (!aligned(p, 16) || ld % 8) return Q4_ERR_ALIGN;
+  return Q4_OK;
+}
+
+// An output bf16 matrix written element by element (2-byte alignment).
+q4_status check_out_bf16(const void* p, int64_t rows, int64_t cols, int64_t ld) {
+  if (rows < 0 || cols < 0) return Q4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return Q4_OK;
+  if (!p) return Q4_ERR_NULL;
+  if (ld < cols) return Q4_ERR_SHAPE;
+  if (!aligned(p, 2)) return Q4_ERR_ALIGN;
+  return Q4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int q4_version(void) { return 100; }
+
+const char* q4_status_string(int status) {
+  switch (status) {
+    case Q4_OK: return "ok";
+    case Q4_ERR_NULL: return "a required pointer is NULL";
+    case Q4_ERR_SHAPE: return "invalid size (negative, too large or not a multiple of the block)";
+    case Q4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case Q4_ERR_FORMAT: return "unknown or unsupported format for this call";
+    case Q4_ERR_HIP: return "HIP launch failed (see q4_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int q4_last_hip_error(void) { return g_last_hip_error; }
+
+q4_status q4_sizes(int fmt, int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes) {
+  const int g = block_of(fmt);
+  if (!g) return Q4_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || cols % g) return Q4_ERR_SHAPE;
+  const size_t elems = (size_t)rows * (size_t)cols;
+  if (codes_bytes) *codes_bytes = elems / 2;
+  if (scales_bytes) *scales_bytes = (size_t)rows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : 1);
+  return Q4_OK;
+}
+
+q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
+                      const float* nv_global_in, void* stream) {
+  q4_status st = check_tensor(dst);
+  if (st != Q4_OK) return st;
+  if (nv_global_in && dst->fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
+  if (nv_global_in && !aligned(nv_global_in, 4)) return Q4_ERR_ALIGN;
+  st = check_bf16(src_bf16, dst->rows, dst->cols, ld);
+  if (st != Q4_OK) return st;
+  if (dst->fmt != Q4_NVFP4 && (dst->rows == 0 || dst->cols == 0)) return Q4_OK;
+  return hip_status(q4::launch_quantize(
+      dst->fmt, static_cast<const uint16_t*>(src_bf16), ld, dst->rows, dst->cols,
+      static_cast<uint8_t*>(dst->codes), dst->scales, dst->global_scale, nv_global_in,
+      as_stream(stream)));
+}
+
+q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld, void* stream) {
+  q4_status st = check_tensor(src);
+  if (st != Q4_OK) return st;
+  if (dst_dtype != 0 && dst_dtype != 1) return Q4_ERR_FORMAT;
+  if (src->rows == 0 || src->cols == 0) return Q4_OK;
+  if (!dst) return Q4_ERR_NULL;
+  if (ld < src->cols) return Q4_ERR_SHAPE;
+  if (!aligned(dst, 16) || ld % (dst_dtype == 0 ? 8 : 4)) return Q4_ERR_ALIGN;
+  return hip_status(q4::launch_dequant(src->fmt, static_cast<const uint8_t*>(src->codes),
+                                       src->scales, src->global_scale, src->rows, src->cols, dst,
+                                       dst_dtype, ld, as_stream(stream)));
+}
+
+q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx, void* y_bf16,
+                  int64_t ldy, void* stream) {
+  q4_status st = check_tensor(W);
+  if (st != Q4_OK) return st;
+  if (B < 0 || B > 16) return Q4_ERR_SHAPE;
+  if (W->cols % 128) return Q4_ERR_SHAPE;
+  if (B == 0 || W->rows == 0) return Q4_OK;
+  if (W->cols == 0) return Q4_ERR_SHAPE;
+  st = check_bf16(x_bf16, B, W->cols, ldx);
+  if (st != Q4_OK) return st;
+  st = check_out_bf16(y_bf16, B, W->rows, ldy);
+  if (st != Q4_OK) return st;
+  return hip_status(q4::launch_gemv(W->fmt, static_cast<const uint8_t*>(W->codes), W->scales,
+                                    W->global_scale, W->rows, W->cols,
+                                    static_cast<const uint16_t*>(x_bf16), ldx, B,
+                                    static_cast<uint16_t*>(y_bf16), ldy, as_stream(stream)));
+}
+
+q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A_q,
+                  const q4_tensor* W, void* C_bf16, int64_t ldc, void* stream) {
+  q4_status st = check_tensor(W);
+  if (st != Q4_OK) return st;
+  if (M < 0 || M >= kMaxDim || M > (int64_t)65535 * 64) return Q4_ERR_SHAPE;
+  if ((A_bf16 == nullptr) == (A_q == nullptr)) return A_bf16 ? Q4_ERR_FORMAT : Q4_ERR_NULL;
+  const int64_t N = W->rows, K = W->cols;
+  if (K % 128) return Q4_ERR_SHAPE;
+  if (A_q) {
+    st = check_tensor(A_q);
+    if (st != Q4_OK) return st;
+    if (A_q->fmt != Q4_MXFP4 || W->fmt != Q4_MXFP4) return Q4_ERR_FORMAT;
+    if (A_q->rows != M || A_q->cols != K) return Q4_ERR_SHAPE;
+  }
+  if (M == 0 || N == 0) return Q4_OK;
+  if (K == 0) return Q4_ERR_SHAPE;
+  if (!A_q) {
+    st = check_bf16(A_bf16, M, K, lda);
+    if (st != Q4_OK) return st;
+  }
+  st = check_out_bf16(C_bf16, M, N, ldc);
+  if (st != Q4_OK) return st;
+  if (A_q)
+    return hip_status(q4::launch_gemm_w4a4(
+        static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,
+        static_cast<const uint8_t*>(W->codes), static_cast<const uint8_t*>(W->scales), N, K,
+        static_cast<uint16_t*>(C_bf16), ldc, as_stream(stream)));
+  return hip_status(q4::launch_gemm_w4a16(W->fmt, static_cast<const uint8_t*>(W->codes),
+                                          W->scales, W->global_scale, N, K,
+                                          static_cast<const uint16_t*>(A_bf16), lda, M,
+                                          static_cast<uint16_t*>(C_bf16), ldc,
+                                          as_stream(stream)));
+}
+
+q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int32_t* gather,
+                          const int32_t* expert_offsets, int32_t E, int64_t P,
+                          const q4_tensor* W, int64_t N, void* C_bf16, int64_t ldc,
+                          void* stream) {
+  q4_status st = check_tensor(W);
+  if (st != Q4_OK) return st;
+  if (E < 0 || E > 65535 || N < 0 || T < 0 || P < 0 || P >= kMaxDim || T >= kMaxDim)
+    return Q4_ERR_SHAPE;
+  if (W->rows != (int64_t)E * N) return Q4_ERR_SHAPE;
+  const int64_t K = W->cols;
+  if (K % 128) return Q4_ERR_SHAPE;
+  if (E == 0 || N == 0 || P == 0) return Q4_OK;
+  if (K == 0) return Q4_ERR_SHAPE;
+  if (!gather || !expert_offsets) return Q4_ERR_NULL;
+  if (!aligned(gather, 4) || !aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
+  st = check_bf16(A_bf16, T, K, lda);
+  if (st != Q4_OK) return st;
+  if (T > 0 && !A_bf16) return Q4_ERR_NULL;
+  st = check_out_bf16(C_bf16, P, N, ldc);
+  if (st != Q4_OK) return st;
+  return hip_status(q4::launch_grouped(W->fmt, static_cast<const uint16_t*>(A_bf16), lda, T,
+                                       gather, expert_offsets, E, P,
+                                       static_cast<const uint8_t*>(W->codes), W->scales,
+                                       W->global_scale, N, K, static_cast<uint16_t*>(C_bf16),
+                                       ldc, as_stream(stream)));
+}
+
+}  // extern "C"

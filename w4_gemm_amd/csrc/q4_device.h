@@ -1,0 +1,89 @@
+// q4_device.h -- device-side number-format helpers for the gfx950 kernels.
+//
+// Bit-level encoders/decoders for the narrow formats the library stores:
+// E2M1 (grid +-{0,0.5,1,1.5,2,3,4,6}), E4M3 (bias 7, max 448, min normal
+// 2^-6, min subnormal 2^-9), E8M0 (power-of-two exponent, bias 127), FP16
+// and BF16.  Every rounding is round-to-nearest, ties to the even code.
+// (Formats: "Quantization in deployment", format cheat sheet and formats.py;
+// "Quantization chains", "E4M3 against E5M2".)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return u2f(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return u2f(pair & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = f2u(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E2M1 code -> value (sign included).
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  // magnitudes 0,0.5,1,1.5,2,3,4,6: exponent field e = bits 2:1, mantissa m = bit 0
+  uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+  float mag = (e == 0) ? 0.5f * (float)m : (float)(2u + m) * (float)(1u << (e - 1)) * 0.5f;
+  return (nib & 8u) ? -mag : mag;
+}
+
+// E4M3 code (sign 0) of t in [0, 448].
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  if (t < 0.015625f) {                        // below 2^-6: subnormal step 2^-9
+    return (uint32_t)__builtin_rintf(t * 512.0f);  // 8 -> 0x08, the min normal
+  }
+  uint32_t u = f2u(t);
+  u += 0x7FFFFu + ((u >> 20) & 1u);          // round mantissa to 3 bits
+  return (u >> 20) - ((127u - 7u) << 3);     // rebias exponent 127 -> 7
+}
+
+// E4M3 code -> fp32 (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;       // m * 2^-9
+  return u2f(((e + 120u) << 23) | (m << 20));
+}
+
+// FP16 bits (sign 0) of t >= 0; >= 65520 gives +inf.
+__device__ __forceinline__ uint32_t fp16_encode(float t) {
+  if (t >= 65520.0f) return 0x7C00u;
+  if (t < 6.103515625e-05f) {                 // below 2^-14: subnormal step 2^-24
+    return (uint32_t)__builtin_rintf(t * 16777216.0f);
+  }
+  uint32_t u = f2u(t);
+  u += 0xFFFu + ((u >> 13) & 1u);             // round mantissa to 10 bits
+  return (u >> 13) - ((127u - 15u) << 10);
+}
+
+// FP16 bits -> fp32 (exact, subnormals included).
+__device__ __forceinline__ float fp16_value(uint32_t h) {
+  uint32_t s = (h & 0x8000u) << 16, e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  if (e == 0) {
+    float v = (float)m * 5.9604644775390625e-08f;  // m * 2^-24
+    return s ? -v : v;
+  }
+  if (e == 31) return u2f(s | 0x7F800000u | (m << 13));
+  return u2f(s | ((e + 112u) << 23) | (m << 13));
+}
+
+// MXFP4 scale exponent for a block whose absmax is amax (fp32, >= 0):
+// floor(log2(max(amax, 1e-12))) - 2, read from the exponent bits (amax is
+// normal once clamped).  Returns the biased E8M0 byte.
+__device__ __forceinline__ uint32_t mx_e8m0(float amax) {
+  float a = fmaxf(amax, 1e-12f);
+  uint32_t biased = (f2u(a) >> 23) & 0xFFu;   // floor(log2 a) + 127
+  return biased - 2u;
+}
+
+// 2^(e - 127) for a biased E8M0 byte e in [1, 254].
+__device__ __forceinline__ float e8m0_value(uint32_t e) { return u2f(e << 23); }
+
+}  // namespace q4

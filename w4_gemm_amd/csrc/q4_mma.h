@@ -1,0 +1,78 @@
+// q4_mma.h -- register-level pieces shared by the W4 matmul kernels on
+// gfx950: vector types, 8-code dequantization to bf16 (the "dequantize
+// weights to BF16 in registers" step of the W4A16 scheme, "Low-bit
+// inference for very large MoE", table "Kernels on different hardware"),
+// and the bf16 matrix-core step.
+#pragma once
+
+#include "q4_device.h"
+
+namespace q4 {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ uint32_t as_u32(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// 8 E2M1 codes (nibble j of `w` is element j) times a power-of-two scale
+// -> 8 bf16, exact.  v_cvt_scalef32_pk_bf16_fp4 converts the two codes of
+// one byte (low nibble first) and applies only the exponent of its fp32
+// scale operand (measured on gfx950: a scale of 1.5 acts as 1.0), which is
+// exactly an E8M0 scale.
+__device__ __forceinline__ bf16x8_t dq8_e2m1(uint32_t w, float scale) {
+  u32x4_t r;
+  r[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return as_bf16x8(r);
+}
+
+// 8 E2M1 codes times an arbitrary fp32 scale (NVFP4: E4M3 * gs) -> 8 bf16:
+// exact fp32 code values, one fp32 multiply, one rounding to bf16.
+__device__ __forceinline__ bf16x8_t dq8_e2m1_mul(uint32_t w, float scale) {
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x2_t v;
+    if (j == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    else if (j == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    else if (j == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    r[j] = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
+  }
+  return as_bf16x8(r);
+}
+
+// 8 INT4 codes (two's complement nibbles) times fp32 scale s -> 8 bf16.
+// Offset-binary trick: nibble ^ 8 = q + 8 in 0..15, read as a byte by
+// v_cvt_f32_ubyte; q*s = (q+8)*s - 8*s is exact in fp32 (<= 15 bits), so
+// one fma gives it; then one rounding to bf16.
+__device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) {
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0,2,4,6
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1,3,5,7
+  const float m8 = -8.0f * s;
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float e0 = __builtin_fmaf((float)((lo >> (8 * j)) & 0xFFu), s, m8);
+    const float e1 = __builtin_fmaf((float)((hi >> (8 * j)) & 0xFFu), s, m8);
+    r[j] = f32_to_bf16_rne(e0) | (f32_to_bf16_rne(e1) << 16);
+  }
+  return as_bf16x8(r);
+}
+
+// bf16 matrix core: C(16x16) += A(16x32) * B(32x16), fp32 accumulation.
+// Lane l supplies A[l%16][8(l/16)..+8] and B[8(l/16)..+8][l%16]; the result
+// lane l, register r holds C[4(l/16)+r][l%16].
+__device__ __forceinline__ f32x4_t mma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace q4

@@ -1,0 +1,290 @@
+// quantize.hip -- round-to-nearest absmax block quantization of bf16 rows
+// into INT4 g128, MXFP4 and NVFP4, and the matching dequantization.
+//
+// Method ("LLM quantization", how quantization works step by step: a
+// group's largest magnitude sets the scale, each value is divided by the
+// scale and rounded; block scaling gives each small group its own scale):
+//   INT4 g128  s = fp16(amax/7); code = clamp(rne(w/s), -8, 7)
+//              ("Low-bit inference for very large MoE", fake_int4)
+//   MXFP4      s = 2^(floor(log2(max(amax,1e-12))) - 2), E8M0 byte;
+//              code = E2M1(clamp(w/s, +-6))  ("Quantization in deployment",
+//              formats.py mxfp4 and fp4)
+//   NVFP4      gs = max(amax_tensor,1e-12)/2688; block code
+//              E4M3(min((amax_b/6)/gs, 448)); code = E2M1(clamp(w/(E4M3*gs)))
+//              (same file, nvfp4)
+//
+// Launch shape: one lane per 8 consecutive values of a row (one 16-byte
+// load, one 4-byte store of packed nibbles).  A block of g values is g/8
+// adjacent lanes (16 for INT4, 4 for MXFP4, 2 for NVFP4); its absmax is a
+// butterfly max over those lanes.  Every lane of a wave runs the same number
+// of iterations so the cross-lane steps see the whole group.
+#include "q4_device.h"
+#include "q4_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace q4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Chunk8 {
+  float v[8];
+};
+
+__device__ __forceinline__ Chunk8 load8(const uint16_t* p, bool valid) {
+  Chunk8 c;
+  uint4 raw = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+  c.v[0] = bf16_lo(raw.x); c.v[1] = bf16_hi(raw.x);
+  c.v[2] = bf16_lo(raw.y); c.v[3] = bf16_hi(raw.y);
+  c.v[4] = bf16_lo(raw.z); c.v[5] = bf16_hi(raw.z);
+  c.v[6] = bf16_lo(raw.w); c.v[7] = bf16_hi(raw.w);
+  return c;
+}
+
+// Eight values -> eight packed E2M1 nibbles (element j in bits 4j..4j+3) of
+// value / scale, with scale a power of two.  v_cvt_scalef32_pk_fp4_f32
+// divides by 2^floor(log2 scale) (only the exponent of its scale operand is
+// used), rounds to the nearest E2M1 value with ties to the even code,
+// saturates to +-6 and keeps the sign bit -- the rounding rule of the
+// formats here, checked on gfx950 against every multiple of 1/128 in
+// [0, 10) including all the midpoints.
+__device__ __forceinline__ uint32_t e2m1_pack8(const Chunk8& c, float scale) {
+  uint32_t p = 0;
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[0], c.v[1], scale, 0);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[2], c.v[3], scale, 1);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[4], c.v[5], scale, 2);
+  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[6], c.v[7], scale, 3);
+  return p;
+}
+
+template <int LANES>
+__device__ __forceinline__ float group_max(float a) {
+#pragma unroll
+  for (int m = 1; m < LANES; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
+  return a;
+}
+
+__device__ __forceinline__ float absmax8(const Chunk8& c) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(c.v[j]));
+  return a;
+}
+
+// FMT: 0 INT4 g128, 1 MXFP4, 2 NVFP4.  For NVFP4, gs_src holds either the
+// global scale (gs_is_amax = 0) or the raw bits of the tensor absmax
+// (gs_is_amax = 1).  gs_out (NVFP4, may equal gs_src only when
+// gs_is_amax = 0) receives gs from the first lane.
+template <int FMT>
+__global__ void __launch_bounds__(kThreads)
+quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+                uint8_t* __restrict__ codes, void* __restrict__ scales,
+                const float* gs_src, int gs_is_amax, float* gs_out) {
+  constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);
+  constexpr int LANES = G / 8;
+  const int64_t cpr = cols >> 3;  // chunks of 8 per row
+  const int64_t total = rows * cpr;
+  const int64_t nblk = cols / G;
+
+  float gs = 0.0f;
+  if constexpr (FMT == 2) {
+    if (gs_is_amax) {
+      gs = fmaxf(u2f(*reinterpret_cast<const uint32_t*>(gs_src)), 1e-12f) / 2688.0f;
+    } else {
+      gs = *gs_src;
+      if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
+    }
+  }
+
+  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < total;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int64_t c = base + threadIdx.x;
+    const bool valid = c < total;
+    const int64_t r = valid ? c / cpr : 0;
+    const int64_t k0 = valid ? (c - r * cpr) * 8 : 0;
+    Chunk8 x = load8(src + r * ld + k0, valid);
+    const float amax = group_max<LANES>(absmax8(x));
+
+    uint32_t packed = 0;
+    if constexpr (FMT == 0) {
+      const uint32_t sbits = fp16_encode(amax / 7.0f);
+      const float s = fp16_value(sbits);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int q = 0;
+        if (s != 0.0f) {
+          float qr = __builtin_rintf(x.v[j] / s);
+          qr = fminf(fmaxf(qr, -8.0f), 7.0f);
+          q = (int)qr;
+        }
+        packed |= ((uint32_t)q & 0xFu) << (4 * j);
+      }
+      if (valid && (k0 % G) == 0)
+        reinterpret_cast<uint16_t*>(scales)[r * nblk + k0 / G] = (uint16_t)sbits;
+    } else if constexpr (FMT == 1) {
+      const uint32_t e = mx_e8m0(amax);
+      packed = e2m1_pack8(x, e8m0_value(e));
+      if (valid && (k0 % G) == 0)
+        reinterpret_cast<uint8_t*>(scales)[r * nblk + k0 / G] = (uint8_t)e;
+    } else {
+      const float t = fminf((amax / 6.0f) / gs, 448.0f);
+      const uint32_t sc = e4m3_encode(t);
+      const float eff = e4m3_value(sc) * gs;
+      if (eff == 0.0f) {  // E4M3 scale underflowed to 0: magnitude codes 0, signs kept
+#pragma unroll
+        for (int j = 0; j < 8; ++j) packed |= ((f2u(x.v[j]) >> 31) << 3) << (4 * j);
+      } else {
+        Chunk8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y.v[j] = x.v[j] / eff;  // fp32 division by the scale as used
+        packed = e2m1_pack8(y, 1.0f);
+      }
+      if (valid && (k0 % G) == 0)
+        reinterpret_cast<uint8_t*>(scales)[r * nblk + k0 / G] = (uint8_t)sc;
+    }
+    if (valid) *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + (k0 >> 1)) = packed;
+  }
+}
+
+// Tensor absmax for NVFP4: max |w| over rows x cols, folded into *amax_bits
+// with an atomic max on the fp32 bits (non-negative floats order like their
+// bit patterns, and max is exact, so the result does not depend on order).
+__global__ void __launch_bounds__(kThreads)
+absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+              uint32_t* amax_bits) {
+  const int64_t cpr = cols >> 3;
+  const int64_t total = rows * cpr;
+  float a = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = c / cpr;
+    const int64_t k0 = (c - r * cpr) * 8;
+    a = fmaxf(a, absmax8(load8(src + r * ld + k0, true)));
+  }
+  a = group_max<64>(a);
+  __shared__ float part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
+    atomicMax(amax_bits, f2u(m));
+  }
+}
+
+__global__ void set_word_kernel(uint32_t* p, uint32_t v) { *p = v; }
+
+// amax bits -> global scale, in place.
+__global__ void finalize_gs_kernel(float* gs) {
+  *gs = fmaxf(u2f(*reinterpret_cast<uint32_t*>(gs)), 1e-12f) / 2688.0f;
+}
+
+// Dequantize: one lane per 8 values; OUT 0 = bf16, 1 = fp32.
+template <int FMT, int OUT>
+__global__ void __launch_bounds__(kThreads)
+dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+               const float* gs_ptr, int64_t rows, int64_t cols, void* __restrict__ dst,
+               int64_t ld) {
+  constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);
+  const int64_t cpr = cols >> 3;
+  const int64_t total = rows * cpr;
+  const int64_t nblk = cols / G;
+  const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = c / cpr;
+    const int64_t k0 = (c - r * cpr) * 8;
+    const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + (k0 >> 1));
+    const int64_t si = r * nblk + k0 / G;
+    float v[8];
+    if constexpr (FMT == 0) {
+      const float s = fp16_value(reinterpret_cast<const uint16_t*>(scales)[si]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = ((int)(packed << (28 - 4 * j))) >> 28;  // sign-extend nibble j
+        v[j] = (float)q * s;
+      }
+    } else if constexpr (FMT == 1) {
+      const float s = e8m0_value(reinterpret_cast<const uint8_t*>(scales)[si]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * s;
+    } else {
+      const float eff = e4m3_value(reinterpret_cast<const uint8_t*>(scales)[si]) * gs;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * eff;
+    }
+    if constexpr (OUT == 0) {
+      uint4 o;
+      o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+      o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
+    } else {
+      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+unsigned grid_for(int64_t chunks) {
+  int64_t b = (chunks + kThreads - 1) / kThreads;
+  if (b < 1) b = 1;
+  if (b > (1 << 20)) b = 1 << 20;
+  return (unsigned)b;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols,
+                           uint8_t* codes, void* scales, float* gs, const float* gs_in,
+                           hipStream_t stream) {
+  const int64_t chunks = rows * (cols >> 3);
+  const unsigned grid = grid_for(chunks);
+  if (fmt == 0) {
+    if (chunks) quantize_kernel<0><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+  } else if (fmt == 1) {
+    if (chunks) quantize_kernel<1><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+  } else {
+    if (gs_in) {
+      if (chunks) {
+        quantize_kernel<2><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs_in, 0, gs);
+      } else {
+        // nothing to quantize: still record the caller's gs
+        hipError_t e = hipMemcpyAsync(gs, gs_in, sizeof(float), hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      uint32_t* amax = reinterpret_cast<uint32_t*>(gs);
+      set_word_kernel<<<1, 1, 0, stream>>>(amax, 0u);
+      if (chunks) {
+        const unsigned agrid = (unsigned)(grid < 2048 ? grid : 2048);
+        absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
+        quantize_kernel<2><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs, 1, nullptr);
+      }
+      finalize_gs_kernel<<<1, 1, 0, stream>>>(gs);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+                          int64_t rows, int64_t cols, void* dst, int dst_dtype, int64_t ld,
+                          hipStream_t stream) {
+  const int64_t chunks = rows * (cols >> 3);
+  if (!chunks) return hipSuccess;
+  const unsigned grid = grid_for(chunks);
+#define Q4_DQ(F, O) dequant_kernel<F, O><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
+  if (dst_dtype == 0) {
+    if (fmt == 0) Q4_DQ(0, 0); else if (fmt == 1) Q4_DQ(1, 0); else Q4_DQ(2, 0);
+  } else {
+    if (fmt == 0) Q4_DQ(0, 1); else if (fmt == 1) Q4_DQ(1, 1); else Q4_DQ(2, 1);
+  }
+#undef Q4_DQ
+  return hipGetLastError();
+}
+
+}  // namespace q4
