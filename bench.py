@@ -51,35 +51,49 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class LaunchTimer:
-    """Average duration of repeated launches of one kind, from HIP events
-    recorded on the launch stream around each launch."""
+class GraphTimer:
+    """Average duration per launch of `fn`: `per_graph` calls are captured
+    into one HIP graph (no host work between the kernels), the graph is
+    replayed `replays` times between two HIP events on the replay stream."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, fn, per_graph=1):
         self.torch = torch
-        self.pairs = []
+        self.per_graph = per_graph
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(per_graph):   # warm the launch path once before capture
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            for i in range(per_graph):
+                fn(i)
+        torch.cuda.synchronize()
 
-    def around(self, fn):
+    def replay_ms(self, replays, warmup=3):
         t = self.torch
+        for _ in range(warmup):
+            self.graph.replay()
+        t.cuda.synchronize()
         s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         s.record()
-        fn()
+        for _ in range(replays):
+            self.graph.replay()
         e.record()
-        self.pairs.append((s, e))
+        t.cuda.synchronize()
+        return s.elapsed_time(e) / replays
 
-    def mean_ms(self):
-        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+    def per_launch_ms(self, replays, warmup=3):
+        return self.replay_ms(replays, warmup) / self.per_graph
 
 
-def timed(torch, fn, iters, warmup):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    lt = LaunchTimer(torch)
-    for _ in range(iters):
-        lt.around(fn)
-    torch.cuda.synchronize()
-    return lt.mean_ms()
+def timed(torch, fn, iters, warmup=1, replays=3):
+    """Average per-launch time of fn() from a graph of `iters` launches,
+    replayed `replays` times after `warmup` untimed replays."""
+    g = GraphTimer(torch, lambda i: fn(), per_graph=iters)
+    return g.per_launch_ms(replays, warmup=warmup)
 
 
 def cpu_cores():
@@ -116,41 +130,46 @@ def main():
     N, K = W.shape
     batches = wl.meta["batches"]
     xs = {b: wl.tensors[f"x{b}"].to(dev) for b in batches}
-    q0 = q4.quantize(W, "mxfp4")
+    q0 = q4.quantize(W, "mxfp4", layout="tiled")
     torch.cuda.synchronize()
     copies = [q0] + [q0.clone() for _ in range(args.copies - 1)]
     wbytes = q0.codes.numel() + q0.scales.numel()
     ys = {b: torch.empty((b, N), dtype=torch.bfloat16, device=dev) for b in batches}
 
-    stream = torch.cuda.current_stream()
-    timers = {b: LaunchTimer(torch) for b in batches}
-    counter = [0]
+    # one step = one GEMV per decode batch; step i uses weight copies
+    # 3i, 3i+1, 3i+2 (mod the number of copies), so consecutive launches never
+    # share a copy.  Steps are captured as HIP graphs and replayed.
+    ncopy = len(copies)
+    nb = len(batches)
+    period = ncopy // __import__("math").gcd(ncopy, nb)   # steps until the copy pattern repeats
 
-    def step(record):
-        for b in batches:
-            Wc = copies[counter[0] % len(copies)]
-            counter[0] += 1
-            if record:
-                timers[b].around(lambda: q4.q4_gemv(Wc, xs[b], ys[b], stream=stream))
-            else:
-                q4.q4_gemv(Wc, xs[b], ys[b], stream=stream)
+    def make_step(i):
+        def run(_):
+            for j, b in enumerate(batches):
+                q4.q4_gemv(copies[(i * nb + j) % ncopy], xs[b], ys[b])
+        return run
 
-    for _ in range(args.warmup):
-        step(False)
+    step_graphs = [GraphTimer(torch, make_step(i)) for i in range(period)]
+    for i in range(args.warmup):
+        step_graphs[i % period].graph.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step_graphs[i % period].graph.replay()
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / args.steps
-    value = len(batches) * wbytes / (ms_per_step * 1e-3) / 1e9
+    value = nb * wbytes / (ms_per_step * 1e-3) / 1e9
 
+    # per-kernel average launch duration: ncopy back-to-back launches of one
+    # batch size on rotating copies, captured and replayed
     per_b = {}
     for b in batches:
-        ms = timers[b].mean_ms()
+        gt = GraphTimer(torch, lambda i, b=b: q4.q4_gemv(copies[i % ncopy], xs[b], ys[b]),
+                        per_graph=ncopy * 4)
+        ms = gt.per_launch_ms(max(3, args.steps // (ncopy * 4)))
         alg = wbytes + b * K * 2 + b * N * 2
         per_b[b] = {"us": ms * 1e3, "weight_GBps": wbytes / (ms * 1e-3) / 1e9,
                     "alg_GBps": alg / (ms * 1e-3) / 1e9, "alg_bytes": alg}
@@ -175,14 +194,24 @@ def main():
                                        for b in batches},
              "weight_copies": len(copies)}
 
+    # the same GEMV on the row-major layout, for comparison
+    rows_copies = [q4.quantize(W, "mxfp4")]
+    rows_copies += [rows_copies[0].clone() for _ in range(args.copies - 1)]
+    extra["decode_gemv_rowmajor_us"] = {}
+    for b in batches:
+        gt = GraphTimer(torch, lambda i, b=b: q4.q4_gemv(rows_copies[i % ncopy], xs[b], ys[b]),
+                        per_graph=ncopy * 4)
+        extra["decode_gemv_rowmajor_us"][str(b)] = round(gt.per_launch_ms(5) * 1e3, 3)
+    del rows_copies
+
     # quantization of the decode weight
-    qt = empty = q4.empty_q4("mxfp4", N, K, device=dev)
+    empty = q4.empty_q4("mxfp4", N, K, device=dev, layout="tiled")
     ms = timed(torch, lambda: q4.q4_quantize(W, empty), 10, 3)
     qbytes = N * K * 2 + wbytes
     extra["quantize_mxfp4_28672x8192"] = {"us": round(ms * 1e3, 2),
                                           "GBps": round(qbytes / (ms * 1e-3) / 1e9, 1),
                                           "bytes": qbytes}
-    del qt, empty
+    del empty
     only = set(filter(None, args.only.split(",")))
 
     def want(name):
@@ -208,7 +237,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "mxfp4_decode_gemv", "N": N, "K": K, "batches": list(batches),
-                   "weight_format": "MXFP4 (E2M1 + E8M0 per 32)", "accumulate": "fp32",
+                   "weight_format": "MXFP4 (E2M1 + E8M0 per 32)", "weight_layout": "tiled 16x128",
+                   "accumulate": "fp32",
                    "global_batch": sum(batches), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -245,7 +275,7 @@ def bench_nvfp4(torch, q4, workloads, dev, seed):
     W = wl.tensors["W"].to(dev)
     M, K = A.shape
     N = W.shape[0]
-    q = q4.quantize(W, "nvfp4")
+    q = q4.quantize(W, "nvfp4", layout="tiled")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ms = timed(torch, lambda: q4.q4_gemm(A, q, C), 10, 2)
     qms = timed(torch, lambda: q4.q4_quantize(W, q), 10, 2)
@@ -263,7 +293,7 @@ def bench_moe(torch, q4, workloads, dev, seed):
     A = wl.tensors["A"].to(dev)
     r = wl.meta["routing"]
     N = wl.meta["N"]
-    q = q4.quantize(W, "mxfp4")
+    q = q4.quantize(W, "mxfp4", layout="tiled")
     del W
     g = torch.from_numpy(r.gather).to(dev)
     o = torch.from_numpy(r.offsets).to(dev)
@@ -286,8 +316,8 @@ def bench_w4a4(torch, q4, workloads, dev, seed):
     W = wl.tensors["W"].to(dev)
     M, K = A.shape
     N = W.shape[0]
-    qw = q4.quantize(W, "mxfp4")
-    qa = q4.quantize(A, "mxfp4")
+    qw = q4.quantize(W, "mxfp4", layout="tiled")
+    qa = q4.quantize(A, "mxfp4", layout="tiled")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ms = timed(torch, lambda: q4.q4_gemm(qa, qw, C), 10, 2)
     ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)

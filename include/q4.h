@@ -21,12 +21,33 @@
  * Every rounding is to nearest, ties to the even code; E2M1 keeps the sign
  * bit of the input; a block whose stored scale is 0 has magnitude codes 0.
  *
- * Layout of a quantized tensor (q4_tensor), all device memory owned by the
- * caller, row-major and dense:
- *   codes   uint8 [rows][cols/2]; element k of a row sits in byte k/2,
- *           even k in bits 3:0, odd k in bits 7:4.  16-byte aligned.
+ * Layouts of a quantized tensor (q4_tensor); all device memory is owned by
+ * the caller.  Within a byte, element k sits in bits 3:0 when k is even and
+ * in bits 7:4 when k is odd.  INT4 codes are 4-bit two's complement; an
+ * E2M1 code is sign*8 + index into {0,0.5,1,1.5,2,3,4,6}.
+ *
+ * Q4_LAYOUT_ROWS (row-major, dense):
+ *   codes   uint8 [rows][cols/2], 16-byte aligned.
  *   scales  INT4: fp16 bits [rows][cols/128]; MXFP4: biased E8M0 exponent
  *           [rows][cols/32]; NVFP4: E4M3 bits [rows][cols/16].  4-byte aligned.
+ *
+ * Q4_LAYOUT_TILED (the weights pre-shuffled so that one 64-lane load is one
+ * contiguous kilobyte holding a whole matrix-core operand; cols % 512 == 0).
+ * Rows are grouped in tiles of 16 (RT = ceil(rows/16) tiles, the last one
+ * padded), K in super-chunks of 128 (S = cols/128) and super-chunks in
+ * groups of four (Q = S/4).  Lane index l = 16*g + n, n = row in the tile
+ * (0..15), g = 32-wide k group in the super-chunk (0..3).
+ *   codes   RT*S tiles of 1024 bytes; tile (t, s) starts at byte
+ *           (t*S + s)*1024 and its bytes [16l, 16l+16) hold the 32 codes
+ *           k = 128s + 32g + j (j = 0..31) of row 16t + n.
+ *   scales  MXFP4: byte ((t*Q + q)*64 + l)*4 + i is the E8M0 of row 16t+n,
+ *                  32-block 4(4q+i) + g                 (RT*Q*256 bytes);
+ *           NVFP4: byte ((t*Q + q)*64 + l)*8 + 2i + h is the E4M3 of row
+ *                  16t+n, 16-block 8(4q+i) + 2g + h    (RT*Q*512 bytes);
+ *           INT4:  fp16 element ((t*Q + q)*16 + n)*4 + i is the scale of
+ *                  row 16t+n, 128-group 4q + i          (RT*Q*128 bytes).
+ *   Padding rows (16t+n >= rows) hold the quantization of zeros.
+ *
  *   global_scale  NVFP4 only: device fp32[1], the multiplier gs; else NULL.
  *
  * Conventions for every call:
@@ -59,6 +80,11 @@ typedef enum q4_format {
     Q4_NVFP4 = 2
 } q4_format;
 
+typedef enum q4_layout {
+    Q4_LAYOUT_ROWS = 0,
+    Q4_LAYOUT_TILED = 1
+} q4_layout;
+
 typedef enum q4_status {
     Q4_OK = 0,
     Q4_ERR_NULL = -1,   /* a required pointer is NULL                      */
@@ -70,11 +96,11 @@ typedef enum q4_status {
 
 typedef struct q4_tensor {
     int32_t fmt;          /* q4_format                                     */
-    int32_t reserved;     /* must be 0                                     */
+    int32_t layout;       /* q4_layout                                     */
     int64_t rows;         /* N for weights, M for activations              */
     int64_t cols;         /* K, a multiple of the format's block size      */
-    void* codes;          /* uint8 [rows][cols/2]                          */
-    void* scales;         /* [rows][cols/g], see above                     */
+    void* codes;          /* packed codes, see the layouts above           */
+    void* scales;         /* block scales, see the layouts above           */
     float* global_scale;  /* NVFP4: fp32[1]; other formats: NULL           */
 } q4_tensor;
 
@@ -88,12 +114,14 @@ const char* q4_status_string(int status);
 int q4_last_hip_error(void);
 
 /*
- * Bytes of codes and scales for a rows x cols tensor of format fmt
- * ("Quantization chains", bits per weight: codes are 4 bits, scales 16/128,
- * 8/32 and 8/16 bits per value).  Either output pointer may be NULL.
- * Q4_ERR_SHAPE if rows < 0, cols < 0 or cols is not a multiple of the block.
+ * Bytes of codes and scales for a rows x cols tensor of format fmt in
+ * layout `layout` ("Quantization chains", bits per weight: codes are 4 bits,
+ * scales 16/128, 8/32 and 8/16 bits per value; the tiled layout adds the
+ * padding of the last row tile).  Either output pointer may be NULL.
+ * Q4_ERR_SHAPE if rows < 0, cols < 0 or cols is not a multiple of the block
+ * (of 512 for the tiled layout); Q4_ERR_FORMAT for an unknown fmt/layout.
  */
-q4_status q4_sizes(int fmt, int64_t rows, int64_t cols, size_t* codes_bytes,
+q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* codes_bytes,
                    size_t* scales_bytes);
 
 /*
@@ -114,8 +142,9 @@ q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
  * Dequantize src into dst [src->rows][ld]: value = fp32(code * scale) with
  * the scale as stored (NVFP4: scale = fp32(E4M3 * gs)).  dst_dtype 0 writes
  * bf16 (the fp32 value rounded to nearest even), 1 writes fp32 (ld a
- * multiple of 4 for fp32).  This is the multiply-back step of
- * "LLM quantization"'s worked example ("divide, round, multiply back").
+ * multiple of 4 for fp32).  This is the step that multiplies the rounded
+ * values back by their scale in the worked example of "LLM quantization".
+ * Either layout is read; the output is always row-major.
  */
 q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld, void* stream);
 

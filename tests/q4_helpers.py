@@ -36,9 +36,32 @@ def scales_np(q, fmt):
     return s.numpy()
 
 
+def untile(codes: np.ndarray, scales: np.ndarray, fmt: str, rows: int, cols: int):
+    """Tiled layout -> row-major (codes [rows, cols/2], scales [rows, cols/g]),
+    following the tiled layout's definition in include/q4.h: tile (t, s) of
+    1 KB holds, at bytes [16l, 16l+16) with l = 16g + n, the codes of row
+    16t+n, k = 128s + 32g .. +32; scales are grouped by four super-chunks."""
+    RT, S = (rows + 15) // 16, cols // 128
+    Q = S // 4
+    c = codes.reshape(RT, S, 4, 16, 16)                 # t, s, g, n, byte
+    c = c.transpose(0, 3, 1, 2, 4).reshape(RT * 16, S * 64)[:rows]
+    if fmt == "mxfp4":
+        sc = scales.reshape(RT, Q, 4, 16, 4)            # t, q, g, n, i
+        sc = sc.transpose(0, 3, 1, 4, 2).reshape(RT * 16, Q * 16)
+    elif fmt == "nvfp4":
+        sc = scales.reshape(RT, Q, 4, 16, 4, 2)         # t, q, g, n, i, h
+        sc = sc.transpose(0, 3, 1, 4, 2, 5).reshape(RT * 16, Q * 32)
+    else:
+        sc = scales.reshape(RT, Q, 16, 4)               # t, q, n, i
+        sc = sc.transpose(0, 2, 1, 3).reshape(RT * 16, Q * 4)
+    return np.ascontiguousarray(c), np.ascontiguousarray(sc[:rows])
+
+
 def assert_quant_equal(q_gpu, q_ref, fmt, rows=None):
     codes = q_gpu.codes.cpu().numpy()
     sc = scales_np(q_gpu, fmt)
+    if q_gpu.layout == 1:
+        codes, sc = untile(codes, sc, fmt, q_gpu.rows, q_gpu.cols)
     if rows is not None:
         codes, sc = codes[rows], sc[rows]
     assert codes.shape == q_ref.codes.shape

@@ -53,18 +53,23 @@ def test_sizes(fmt, cols, codes, scales):
     assert q4.q4_sizes(fmt, 1, cols) == (codes, scales)
     assert q4.q4_sizes(fmt, 28672, 8192)[0] == 28672 * 4096
     assert q4.q4_sizes(fmt, 0, cols) == (0, 0)
+    # tiled: whole 16-row tiles, the same bytes per stored row
+    assert q4.q4_sizes(fmt, 1, cols, "tiled") == (16 * codes, 16 * scales)
+    assert q4.q4_sizes(fmt, 32, cols, "tiled") == (32 * codes, 32 * scales)
 
 
 def test_sizes_rejects():
     L = q4.lib()
-    assert L.q4_sizes(7, 1, 128, None, None) == FMT
-    assert L.q4_sizes(q4.MXFP4, 1, 48, None, None) == SHAPE
-    assert L.q4_sizes(q4.INT4_G128, 1, 64, None, None) == SHAPE
-    assert L.q4_sizes(q4.MXFP4, -1, 64, None, None) == SHAPE
+    assert L.q4_sizes(7, 0, 1, 128, None, None) == FMT
+    assert L.q4_sizes(q4.MXFP4, 5, 1, 128, None, None) == FMT
+    assert L.q4_sizes(q4.MXFP4, 0, 1, 48, None, None) == SHAPE
+    assert L.q4_sizes(q4.INT4_G128, 0, 1, 64, None, None) == SHAPE
+    assert L.q4_sizes(q4.MXFP4, 0, -1, 64, None, None) == SHAPE
+    assert L.q4_sizes(q4.MXFP4, 1, 1, 256, None, None) == SHAPE   # tiled: cols % 512
 
 
-def desc(fmt=q4.MXFP4, rows=64, cols=256, codes=A16, scales=A16, gs=None, reserved=0):
-    return q4._Q4TensorC(fmt, reserved, rows, cols, codes, scales, gs)
+def desc(fmt=q4.MXFP4, rows=64, cols=256, codes=A16, scales=A16, gs=None, layout=0):
+    return q4._Q4TensorC(fmt, layout, rows, cols, codes, scales, gs)
 
 
 def call_quantize(src, ld, d, gs_in=None):
@@ -76,7 +81,9 @@ def test_quantize_validation():
     assert L.q4_quantize(A16, 256, None, None, None) == NULL
     assert call_quantize(None, 256, desc()) == NULL
     assert call_quantize(A16, 256, desc(fmt=9)) == FMT
-    assert call_quantize(A16, 256, desc(reserved=1)) == FMT
+    assert call_quantize(A16, 256, desc(layout=2)) == FMT
+    assert call_quantize(A16, 256, desc(layout=1)) == SHAPE       # tiled needs cols % 512
+    assert call_quantize(A16, 512, desc(layout=1, cols=512, rows=0)) == OK
     assert call_quantize(A16, 256, desc(cols=48)) == SHAPE
     assert call_quantize(A16, 256, desc(rows=-1)) == SHAPE
     assert call_quantize(A16, 128, desc()) == SHAPE              # ld < cols
@@ -150,3 +157,4 @@ def test_grouped_validation():
     assert call(ldc=100) == SHAPE
     assert call(P=0) == OK
     assert call(W=desc(rows=8 * 128, cols=96), N=128) == SHAPE
+    assert call(W=desc(rows=8 * 120, cols=512, layout=1), N=120) == SHAPE  # tiled: N % 16

@@ -18,21 +18,31 @@ FMTS = ("int4", "mxfp4", "nvfp4")
 EXACT = {"int4": False, "mxfp4": True, "nvfp4": False}
 
 
-def quantized(w_bf16, fmt):
-    qg = q4.quantize(w_bf16.to(DEV), fmt)
+def quantized(w_bf16, fmt, layout="rows"):
+    qg = q4.quantize(w_bf16.to(DEV), fmt, layout=layout)
     qr = oracle.quantize(fmt, to_f32(w_bf16))
     return qg, qr
+
+
+def tiled_ok(K, rows=16):
+    return K % 512 == 0 and rows % 16 == 0
+
+
+LAYOUTS = ("rows", "tiled")
 
 
 # --------------------------------------------------------------------------
 # GEMV
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("N,K", [(1000, 1024), (77, 384), (4100, 1280), (16400, 2048)])
-def test_gemv_small(fmt, N, K):
-    log("gemv", fmt, N, K)
+@pytest.mark.parametrize("N,K", [(1000, 1024), (77, 384), (4100, 1280), (16400, 2048), (40, 512)])
+def test_gemv_small(fmt, N, K, layout):
+    if layout == "tiled" and not tiled_ok(K):
+        pytest.skip("the tiled layout needs K % 512 == 0")
+    log("gemv", fmt, layout, N, K)
     w = workloads.matrix(f"tg/w{N}x{K}", N, K, 0.02, seed=21, outlier_frac=0.001, outlier_mult=20.0)
-    qg, qr = quantized(w, fmt)
+    qg, qr = quantized(w, fmt, layout)
     wd = oracle.dequant(qr)
     for B in (1, 3, 16):
         x = workloads.matrix(f"tg/x{B}x{K}", B, K, 1.0, seed=22)
@@ -45,11 +55,12 @@ def test_gemv_small(fmt, N, K):
         check_matmul(yc[:, :N], ref, to_f32(x), wd, EXACT[fmt], f"gemv {fmt} B={B}")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-def test_gemv_one_hot_x_returns_a_column(fmt):
+def test_gemv_one_hot_x_returns_a_column(fmt, layout):
     N, K = 300, 512
     w = workloads.matrix("tg/onehot", N, K, 0.05, seed=23)
-    qg, qr = quantized(w, fmt)
+    qg, qr = quantized(w, fmt, layout)
     wd = oracle.dequant(qr)
     for k in (0, 129, 511):
         x = torch.zeros((1, K), dtype=torch.bfloat16)
@@ -64,23 +75,25 @@ def test_gemv_one_hot_x_returns_a_column(fmt):
         assert np.array_equal(got, exp)
 
 
-def test_gemv_all_ones_accumulates_in_fp32():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_all_ones_accumulates_in_fp32(layout):
     """All-ones weights and x over K = 1024 must give exactly 1024; a bf16
     accumulator would stop at 256."""
     K = 1024
     w = torch.ones((64, K), dtype=torch.bfloat16)
-    qg, _ = quantized(w, "mxfp4")
+    qg, _ = quantized(w, "mxfp4", layout)
     y = torch.empty((1, 64), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemv(qg, torch.ones((1, K), dtype=torch.bfloat16, device=DEV), y)
     torch.cuda.synchronize()
     assert torch.all(y.cpu().float() == 1024.0)
 
 
-def test_gemv_batch_rows_are_independent():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_batch_rows_are_independent(layout):
     """Row b of a B=16 GEMV equals the B=1 GEMV of that row, bit for bit."""
     N, K = 2048, 2048
     w = workloads.matrix("tg/batch", N, K, 0.02, seed=24)
-    qg, _ = quantized(w, "mxfp4")
+    qg, _ = quantized(w, "mxfp4", layout)
     x = workloads.matrix("tg/batchx", 16, K, 1.0, seed=25).to(DEV)
     y16 = torch.empty((16, N), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemv(qg, x, y16)
@@ -91,10 +104,11 @@ def test_gemv_batch_rows_are_independent():
         assert torch.equal(y1[0], y16[b])
 
 
-def test_gemv_deterministic():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_deterministic(layout):
     N, K = 4096, 4096
     w = workloads.matrix("tg/det", N, K, 0.02, seed=26)
-    qg, _ = quantized(w, "mxfp4")
+    qg, _ = quantized(w, "mxfp4", layout)
     x = workloads.matrix("tg/detx", 4, K, 1.0, seed=27).to(DEV)
     a = torch.empty((4, N), dtype=torch.bfloat16, device=DEV)
     b = torch.empty((4, N), dtype=torch.bfloat16, device=DEV)
@@ -104,9 +118,10 @@ def test_gemv_deterministic():
     assert torch.equal(a, b)
 
 
-def test_full_int4_gemv():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_int4_gemv(layout):
     wl = workloads.int4_gemv()
-    qg, qr = quantized(wl.tensors["W"], "int4")
+    qg, qr = quantized(wl.tensors["W"], "int4", layout)
     x = wl.tensors["x"]
     y = torch.empty((1, 1024), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemv(qg, x.to(DEV), y)
@@ -116,14 +131,15 @@ def test_full_int4_gemv():
     log("int4 g128 gemv max normalized error", e)
 
 
-def test_full_mxfp4_decode_gemv():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_mxfp4_decode_gemv(layout):
     """28672 x 8192 MXFP4, B = 1, 4, 16: 512 sampled output columns n (all
-    batch rows) against the oracle."""
+    batch rows) against the oracle; the tiled case is the benchmark's."""
     wl = workloads.mxfp4_gemv()
     W = wl.tensors["W"]
     N, K = W.shape
-    log("mxfp4 decode gemv: quantize")
-    qg = q4.quantize(W.to(DEV), "mxfp4")
+    log("mxfp4 decode gemv: quantize", layout)
+    qg = q4.quantize(W.to(DEV), "mxfp4", layout=layout)
     rows = np.sort(np.random.default_rng(28).choice(N, 512, replace=False))
     rows[:3] = [0, N // 2, N - 1]
     rows = np.unique(rows)
@@ -143,13 +159,16 @@ def test_full_mxfp4_decode_gemv():
 # --------------------------------------------------------------------------
 # W4A16 GEMM
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (1, 1000, 1024), (333, 520, 1152)])
-def test_gemm_w4a16_small(fmt, M, N, K):
-    log("gemm w4a16", fmt, M, N, K)
+def test_gemm_w4a16_small(fmt, M, N, K, layout):
+    if layout == "tiled" and not tiled_ok(K):
+        pytest.skip("the tiled layout needs K % 512 == 0")
+    log("gemm w4a16", fmt, layout, M, N, K)
     w = workloads.matrix(f"tm/w{N}x{K}", N, K, 0.02, seed=31)
     a = workloads.matrix(f"tm/a{M}x{K}", M, K, 1.0, seed=32, channel_frac=0.01, channel_mult=10.0)
-    qg, qr = quantized(w, fmt)
+    qg, qr = quantized(w, fmt, layout)
     C = torch.full((M, N + 4), float("nan"), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemm(a.to(DEV), qg, C[:, :N])
     torch.cuda.synchronize()
@@ -160,14 +179,15 @@ def test_gemm_w4a16_small(fmt, M, N, K):
                  f"w4a16 {fmt}")
 
 
-def test_full_nvfp4_prefill_gemm():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_full_nvfp4_prefill_gemm(layout):
     """4096 x 8192 x 8192 with NVFP4 weights: 64 sampled rows of C (all 8192
     columns) against the oracle."""
     wl = workloads.nvfp4_gemm()
     A, W = wl.tensors["A"], wl.tensors["W"]
     M, N = A.shape[0], W.shape[0]
-    log("nvfp4 prefill: quantize")
-    qg, qr = quantized(W, "nvfp4")
+    log("nvfp4 prefill: quantize", layout)
+    qg, qr = quantized(W, "nvfp4", layout)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemm(A.to(DEV), qg, C)
     torch.cuda.synchronize()
@@ -182,13 +202,17 @@ def test_full_nvfp4_prefill_gemm():
 # --------------------------------------------------------------------------
 # W4A4 MXFP4 GEMM
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("alayout,wlayout", [("rows", "rows"), ("tiled", "tiled"),
+                                             ("rows", "tiled"), ("tiled", "rows")])
 @pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (129, 1000, 1024)])
-def test_gemm_w4a4_small(M, N, K):
-    log("gemm w4a4", M, N, K)
+def test_gemm_w4a4_small(M, N, K, alayout, wlayout):
+    if "tiled" in (alayout, wlayout) and not tiled_ok(K):
+        pytest.skip("the tiled layout needs K % 512 == 0")
+    log("gemm w4a4", alayout, wlayout, M, N, K)
     w = workloads.matrix(f"t4/w{N}x{K}", N, K, 0.02, seed=41)
     a = workloads.matrix(f"t4/a{M}x{K}", M, K, 1.0, seed=42)
-    qw, qwr = quantized(w, "mxfp4")
-    qa, qar = quantized(a, "mxfp4")
+    qw, qwr = quantized(w, "mxfp4", wlayout)
+    qa, qar = quantized(a, "mxfp4", alayout)
     C = torch.full((M, N + 4), float("nan"), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemm(qa, qw, C[:, :N])
     torch.cuda.synchronize()
@@ -198,11 +222,12 @@ def test_gemm_w4a4_small(M, N, K):
     check_matmul(Cc[:, :N], oracle.gemm_w4a4(None, qwr, aq=qar), ad, wd, True, "w4a4")
 
 
-def test_w4a4_identity_a_returns_w_transposed():
-    K = 256
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_w4a4_identity_a_returns_w_transposed(layout):
+    K = 512
     w = workloads.matrix("t4/id", 128, K, 0.05, seed=43)
-    qw, qwr = quantized(w, "mxfp4")
-    qa, _ = quantized(torch.eye(K, dtype=torch.bfloat16), "mxfp4")
+    qw, qwr = quantized(w, "mxfp4", layout)
+    qa, _ = quantized(torch.eye(K, dtype=torch.bfloat16), "mxfp4", layout)
     C = torch.empty((K, 128), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemm(qa, qw, C)
     torch.cuda.synchronize()
@@ -216,9 +241,9 @@ def test_full_w4a4_gemm():
     wl = workloads.w4a4_gemm()
     A, W = wl.tensors["A"], wl.tensors["W"]
     M, N = A.shape[0], W.shape[0]
-    log("w4a4: quantize")
-    qw, qwr = quantized(W, "mxfp4")
-    qa = q4.quantize(A.to(DEV), "mxfp4")
+    log("w4a4: quantize (tiled, the benchmark's layout)")
+    qw, qwr = quantized(W, "mxfp4", "tiled")
+    qa = q4.quantize(A.to(DEV), "mxfp4", layout="tiled")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     q4.q4_gemm(qa, qw, C)
     torch.cuda.synchronize()
@@ -240,12 +265,16 @@ def _grouped_case(E, N, K, T, topk, seed, fmt="mxfp4"):
     return w, a, workloads.route(logits, topk)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("E,N,K,T,topk", [(8, 200, 512, 50, 2), (16, 128, 256, 300, 4), (4, 72, 128, 3, 1)])
-def test_grouped_small(fmt, E, N, K, T, topk):
-    log("grouped", fmt, E, N, K, T, topk)
+@pytest.mark.parametrize("E,N,K,T,topk", [(8, 200, 512, 50, 2), (16, 128, 256, 300, 4),
+                                          (4, 72, 128, 3, 1), (8, 144, 1024, 70, 3)])
+def test_grouped_small(fmt, E, N, K, T, topk, layout):
+    if layout == "tiled" and not tiled_ok(K, N):
+        pytest.skip("the tiled layout needs K % 512 == 0 and N % 16 == 0")
+    log("grouped", fmt, layout, E, N, K, T, topk)
     w, a, r = _grouped_case(E, N, K, T, topk, 51)
-    qg, qr = quantized(w, fmt)
+    qg, qr = quantized(w, fmt, layout)
     P = len(r.gather)
     C = torch.full((P, N + 2), float("nan"), dtype=torch.bfloat16, device=DEV)
     q4.q4_grouped_gemm(a.to(DEV), torch.from_numpy(r.gather).to(DEV),
@@ -291,8 +320,8 @@ def test_full_moe_grouped():
     wl = workloads.moe_grouped()
     W, A, r = wl.tensors["W"], wl.tensors["A"], wl.meta["routing"]
     N = wl.meta["N"]
-    log("moe: quantize")
-    qg = q4.quantize(W.to(DEV), "mxfp4")
+    log("moe: quantize (tiled, the benchmark's layout)")
+    qg = q4.quantize(W.to(DEV), "mxfp4", layout="tiled")
     P = len(r.gather)
     C = torch.empty((P, N), dtype=torch.bfloat16, device=DEV)
     q4.q4_grouped_gemm(A.to(DEV), torch.from_numpy(r.gather).to(DEV),

@@ -15,10 +15,10 @@ FMTS = ("int4", "mxfp4", "nvfp4")
 DEV = "cuda:0"
 
 
-def quant_both(w_bf16: torch.Tensor, fmt: str, gs=None):
+def quant_both(w_bf16: torch.Tensor, fmt: str, gs=None, layout="rows"):
     wd = w_bf16.to(DEV)
     gs_t = None if gs is None else torch.tensor([gs], dtype=torch.float32, device=DEV)
-    qg = q4.quantize(wd, fmt, nv_global_in=gs_t)
+    qg = q4.quantize(wd, fmt, nv_global_in=gs_t, layout=layout)
     torch.cuda.synchronize()
     qr = oracle.quantize(fmt, to_f32(w_bf16), gs=gs)
     return qg, qr
@@ -36,7 +36,26 @@ def test_quantize_small_random(fmt, shape):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_quantize_all_bf16_values(fmt):
+@pytest.mark.parametrize("shape", [(1, 512), (16, 512), (37, 1024), (130, 1536), (257, 512)])
+def test_quantize_small_random_tiled(fmt, shape):
+    log("quantize tiled", fmt, shape)
+    rows, cols = shape
+    w = workloads.matrix(f"tq/t{rows}x{cols}", rows, cols, 0.02, seed=17,
+                         outlier_frac=0.002, outlier_mult=25.0)
+    qg, qr = quant_both(w, fmt, layout="tiled")
+    assert_quant_equal(qg, qr, fmt)
+    # the padding rows of the last tile hold the quantization of zeros
+    pad = (-rows) % 16
+    if pad:
+        zq = oracle.quantize(fmt, np.zeros((16, cols), np.float32))
+        from q4_helpers import scales_np, untile
+        c, sc = untile(qg.codes.cpu().numpy(), scales_np(qg, fmt), fmt, rows + pad, cols)
+        assert np.array_equal(c[rows:], zq.codes[:pad]) and np.array_equal(sc[rows:], zq.scales[:pad])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("layout", ("rows", "tiled"))
+def test_quantize_all_bf16_values(fmt, layout):
     """Every finite bf16 bit pattern, grouped into blocks in three different
     orders so each value meets many block scales."""
     bits = np.arange(0, 1 << 16, dtype=np.uint32)
@@ -54,8 +73,8 @@ def test_quantize_all_bf16_values(fmt):
             x = x[: (x.size // 16) * 16].reshape(-1, 16)[:, ::-1].reshape(-1).copy()
         n = (x.size // 1024) * 1024
         w = torch.from_numpy(x[:n].reshape(-1, 1024)).to(torch.bfloat16)
-        log("all bf16", fmt, order, tuple(w.shape))
-        qg, qr = quant_both(w, fmt)
+        log("all bf16", fmt, layout, order, tuple(w.shape))
+        qg, qr = quant_both(w, fmt, layout=layout)
         assert_quant_equal(qg, qr, fmt)
 
 
@@ -80,20 +99,21 @@ def test_quantize_exact_ties(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_quantize_edge_blocks(fmt):
-    w = np.zeros((8, 256), np.float32)
+@pytest.mark.parametrize("layout", ("rows", "tiled"))
+def test_quantize_edge_blocks(fmt, layout):
+    w = np.zeros((8, 512), np.float32)
     w[1] = -0.0
     w[2, :] = 1e-30                      # below the 1e-12 clamp
     w[3, ::2] = 3.0e38                   # near the top of fp32 (MX, NV only)
     w[4, :] = np.float32(2.0 ** -130)    # bf16 subnormal
     w[5, 7] = 1.0                        # one nonzero per block
-    w[6, :] = np.linspace(-1, 1, 256)
-    w[7, :] = 448.0 * 6 * np.sign(np.linspace(-1, 1, 256))
+    w[6, :] = np.linspace(-1, 1, 512)
+    w[7, :] = 448.0 * 6 * np.sign(np.linspace(-1, 1, 512))
     if fmt == "int4":
         w[3] = 0.0
         w[7] = np.sign(w[7]) * 1000.0
     wt = torch.from_numpy(w).to(torch.bfloat16)
-    qg, qr = quant_both(wt, fmt)
+    qg, qr = quant_both(wt, fmt, layout=layout)
     assert_quant_equal(qg, qr, fmt)
 
 
@@ -127,18 +147,20 @@ def test_quantize_strided_source_and_empty():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_dequant_bit_exact(fmt):
-    w = workloads.matrix("tq/dq", 96, 768, 0.03, seed=15, outlier_frac=0.01, outlier_mult=30.0)
-    qg, qr = quant_both(w, fmt)
+@pytest.mark.parametrize("layout,rows,cols", [("rows", 96, 768), ("tiled", 90, 1024)])
+def test_dequant_bit_exact(fmt, layout, rows, cols):
+    w = workloads.matrix(f"tq/dq{cols}", rows, cols, 0.03, seed=15, outlier_frac=0.01,
+                         outlier_mult=30.0)
+    qg, qr = quant_both(w, fmt, layout=layout)
     ref = oracle.dequant(qr)
-    out32 = torch.full((96, 776), float("nan"), device=DEV)
-    q4.q4_dequant(qg, out32[:, :768])
-    out16 = torch.empty((96, 768), dtype=torch.bfloat16, device=DEV)
+    out32 = torch.full((rows, cols + 8), float("nan"), device=DEV)
+    q4.q4_dequant(qg, out32[:, :cols])
+    out16 = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
     q4.q4_dequant(qg, out16)
     torch.cuda.synchronize()
     o32 = out32.cpu().numpy()
-    assert np.array_equal(o32[:, :768].view(np.uint32), ref.view(np.uint32))
-    assert np.all(np.isnan(o32[:, 768:]))         # nothing written past cols
+    assert np.array_equal(o32[:, :cols].view(np.uint32), ref.view(np.uint32))
+    assert np.all(np.isnan(o32[:, cols:]))        # nothing written past cols
     o16 = out16.cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(o16, oracle.f32_to_bf16_bits(ref))
 
@@ -160,25 +182,27 @@ def test_full_int4_gemv_weight():
     assert_quant_equal(qg, qr, "int4")
 
 
-def test_full_mxfp4_decode_weight():
+@pytest.mark.parametrize("layout", ("rows", "tiled"))
+def test_full_mxfp4_decode_weight(layout):
     wl = workloads.mxfp4_gemv(batches=(1,))
-    log("quantize 28672x8192 MXFP4")
-    qg, qr = quant_both(wl.tensors["W"], "mxfp4")
+    log("quantize 28672x8192 MXFP4", layout)
+    qg, qr = quant_both(wl.tensors["W"], "mxfp4", layout=layout)
     assert_quant_equal(qg, qr, "mxfp4")
 
 
-def test_full_nvfp4_prefill_weight():
+@pytest.mark.parametrize("layout", ("rows", "tiled"))
+def test_full_nvfp4_prefill_weight(layout):
     wl = workloads.nvfp4_gemm()
-    log("quantize 8192x8192 NVFP4")
-    qg, qr = quant_both(wl.tensors["W"], "nvfp4")
+    log("quantize 8192x8192 NVFP4", layout)
+    qg, qr = quant_both(wl.tensors["W"], "nvfp4", layout=layout)
     assert_quant_equal(qg, qr, "nvfp4")
 
 
 def test_full_w4a4_operands():
     wl = workloads.w4a4_gemm()
     for name in ("A", "W"):
-        log("quantize 8192x8192 MXFP4", name)
-        qg, qr = quant_both(wl.tensors[name], "mxfp4")
+        log("quantize 8192x8192 MXFP4 tiled", name)
+        qg, qr = quant_both(wl.tensors[name], "mxfp4", layout="tiled")
         assert_quant_equal(qg, qr, "mxfp4")
 
 
@@ -188,8 +212,8 @@ def test_full_moe_experts_weight():
     wl = workloads.moe_grouped()
     W = wl.tensors["W"]
     N = wl.meta["N"]
-    log("quantize 64x2048x7168 MXFP4")
-    qg = q4.quantize(W.to(DEV), "mxfp4")
+    log("quantize 64x2048x7168 MXFP4 tiled")
+    qg = q4.quantize(W.to(DEV), "mxfp4", layout="tiled")
     torch.cuda.synchronize()
     for e in (0, 21, 42, 63):
         rows = np.arange(e * N, (e + 1) * N)

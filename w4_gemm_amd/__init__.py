@@ -18,12 +18,15 @@ import torch
 
 __all__ = [
     "INT4_G128", "MXFP4", "NVFP4", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
+    "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
     "q4_grouped_gemm", "empty_q4", "quantize", "LIB_PATH",
 ]
 
 INT4_G128, MXFP4, NVFP4 = 0, 1, 2
 FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4}
+LAYOUT_ROWS, LAYOUT_TILED = 0, 1
+LAYOUT_NAMES = {"rows": LAYOUT_ROWS, "tiled": LAYOUT_TILED}
 GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +46,7 @@ class Q4Error(RuntimeError):
 class _Q4TensorC(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
         ("rows", ctypes.c_int64),
         ("cols", ctypes.c_int64),
         ("codes", ctypes.c_void_p),
@@ -68,7 +71,7 @@ def _lib_handle():
             "q4_version": ([], ctypes.c_int),
             "q4_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "q4_last_hip_error": ([], ctypes.c_int),
-            "q4_sizes": ([ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_size_t),
+            "q4_sizes": ([ctypes.c_int, ctypes.c_int, i64, i64, ctypes.POINTER(ctypes.c_size_t),
                           ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "q4_quantize": ([vp, i64, P, vp, vp], ctypes.c_int),
             "q4_dequant": ([P, vp, ctypes.c_int, i64, vp], ctypes.c_int),
@@ -111,13 +114,20 @@ def _fmt(fmt) -> int:
     return FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
 
 
+def _layout(layout) -> int:
+    return LAYOUT_NAMES[layout] if isinstance(layout, str) else int(layout)
+
+
 @dataclass
 class Q4Tensor:
     """A quantized matrix: rows x cols values, blocks along cols.
 
-    codes  uint8 [rows, cols/2]   (even k in the low nibble)
-    scales INT4: int16 (fp16 bits) [rows, cols/128]; MXFP4: uint8 (E8M0)
-           [rows, cols/32]; NVFP4: uint8 (E4M3) [rows, cols/16]
+    Row-major layout (LAYOUT_ROWS):
+      codes  uint8 [rows, cols/2]   (even k in the low nibble)
+      scales INT4: int16 (fp16 bits) [rows, cols/128]; MXFP4: uint8 (E8M0)
+             [rows, cols/32]; NVFP4: uint8 (E4M3) [rows, cols/16]
+    Tiled layout (LAYOUT_TILED, cols % 512 == 0): the same bytes arranged in
+      16-row x 128-column tiles (include/q4.h); the tensors here are flat.
     global_scale  NVFP4: float32 [1] (dequant multiplier); else None
     """
     fmt: int
@@ -126,9 +136,10 @@ class Q4Tensor:
     codes: torch.Tensor
     scales: torch.Tensor
     global_scale: Optional[torch.Tensor] = None
+    layout: int = LAYOUT_ROWS
 
     def c(self) -> _Q4TensorC:
-        return _Q4TensorC(self.fmt, 0, self.rows, self.cols,
+        return _Q4TensorC(self.fmt, self.layout, self.rows, self.cols,
                           self.codes.data_ptr() if self.codes.numel() else None,
                           self.scales.data_ptr() if self.scales.numel() else None,
                           None if self.global_scale is None else self.global_scale.data_ptr())
@@ -140,33 +151,36 @@ class Q4Tensor:
 
     def clone(self) -> "Q4Tensor":
         return Q4Tensor(self.fmt, self.rows, self.cols, self.codes.clone(), self.scales.clone(),
-                        None if self.global_scale is None else self.global_scale.clone())
+                        None if self.global_scale is None else self.global_scale.clone(),
+                        self.layout)
 
 
 def q4_version() -> int:
     return lib().q4_version()
 
 
-def q4_sizes(fmt, rows: int, cols: int):
+def q4_sizes(fmt, rows: int, cols: int, layout=LAYOUT_ROWS):
     """(codes bytes, scales bytes) of a rows x cols tensor."""
     cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib().q4_sizes(_fmt(fmt), rows, cols, ctypes.byref(cb), ctypes.byref(sb)), "q4_sizes")
+    _check(lib().q4_sizes(_fmt(fmt), _layout(layout), rows, cols, ctypes.byref(cb),
+                          ctypes.byref(sb)), "q4_sizes")
     return cb.value, sb.value
 
 
-def empty_q4(fmt, rows: int, cols: int, device="cuda") -> Q4Tensor:
+def empty_q4(fmt, rows: int, cols: int, device="cuda", layout=LAYOUT_ROWS) -> Q4Tensor:
     """Allocate (with torch) the buffers of a quantized tensor."""
-    f = _fmt(fmt)
-    cb, sb = q4_sizes(f, rows, cols)
-    codes = torch.empty(cb, dtype=torch.uint8, device=device).view(rows, cols // 2) \
-        if rows and cols else torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+    f, lay = _fmt(fmt), _layout(layout)
+    cb, sb = q4_sizes(f, rows, cols, lay)
     g = GROUP[f]
-    if f == INT4_G128:
-        scales = torch.empty((rows, cols // g), dtype=torch.int16, device=device)
+    sdt = torch.int16 if f == INT4_G128 else torch.uint8
+    if lay == LAYOUT_ROWS:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, cols // g), dtype=sdt, device=device)
     else:
-        scales = torch.empty((rows, cols // g), dtype=torch.uint8, device=device)
+        codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        scales = torch.empty(sb // (2 if f == INT4_G128 else 1), dtype=sdt, device=device)
     gs = torch.empty(1, dtype=torch.float32, device=device) if f == NVFP4 else None
-    return Q4Tensor(f, rows, cols, codes, scales, gs)
+    return Q4Tensor(f, rows, cols, codes, scales, gs, lay)
 
 
 def q4_quantize(src: torch.Tensor, dst: Q4Tensor, nv_global_in: Optional[torch.Tensor] = None,
@@ -181,9 +195,9 @@ def q4_quantize(src: torch.Tensor, dst: Q4Tensor, nv_global_in: Optional[torch.T
 
 
 def quantize(src: torch.Tensor, fmt, nv_global_in: Optional[torch.Tensor] = None,
-             stream=None) -> Q4Tensor:
+             stream=None, layout=LAYOUT_ROWS) -> Q4Tensor:
     """Allocate a Q4Tensor on src's device and quantize src into it."""
-    dst = empty_q4(fmt, src.shape[0], src.shape[1], device=src.device)
+    dst = empty_q4(fmt, src.shape[0], src.shape[1], device=src.device, layout=layout)
     return q4_quantize(src, dst, nv_global_in, stream)
 
 

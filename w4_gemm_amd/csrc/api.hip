@@ -30,14 +30,15 @@ q4_status hip_status(hipError_t e) {
   return Q4_ERR_HIP;
 }
 
-// Validates a quantized tensor descriptor.  With `need_data` the codes,
-// scales (and NVFP4 global scale) must be present.
+// Validates a quantized tensor descriptor: known format and layout, sizes
+// in range and multiples of the block (of 512 in the tiled layout), buffers
+// present and aligned when the tensor is not empty.
 q4_status check_tensor(const q4_tensor* t) {
   if (!t) return Q4_ERR_NULL;
   const int g = block_of(t->fmt);
-  if (!g || t->reserved != 0) return Q4_ERR_FORMAT;
+  if (!g || (t->layout != Q4_LAYOUT_ROWS && t->layout != Q4_LAYOUT_TILED)) return Q4_ERR_FORMAT;
   if (t->rows < 0 || t->cols < 0 || t->rows >= kMaxDim || t->cols >= kMaxDim) return Q4_ERR_SHAPE;
-  if (t->cols % g) return Q4_ERR_SHAPE;
+  if (t->cols % (t->layout == Q4_LAYOUT_TILED ? 512 : g)) return Q4_ERR_SHAPE;
   if (t->fmt == Q4_NVFP4) {
     if (!t->global_scale) return Q4_ERR_NULL;
     if (!aligned(t->global_scale, 4)) return Q4_ERR_ALIGN;
@@ -93,13 +94,17 @@ const char* q4_status_string(int status) {
 
 int q4_last_hip_error(void) { return g_last_hip_error; }
 
-q4_status q4_sizes(int fmt, int64_t rows, int64_t cols, size_t* codes_bytes, size_t* scales_bytes) {
+q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* codes_bytes,
+                   size_t* scales_bytes) {
   const int g = block_of(fmt);
-  if (!g) return Q4_ERR_FORMAT;
-  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim || cols % g) return Q4_ERR_SHAPE;
-  const size_t elems = (size_t)rows * (size_t)cols;
-  if (codes_bytes) *codes_bytes = elems / 2;
-  if (scales_bytes) *scales_bytes = (size_t)rows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : 1);
+  if (!g || (layout != Q4_LAYOUT_ROWS && layout != Q4_LAYOUT_TILED)) return Q4_ERR_FORMAT;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return Q4_ERR_SHAPE;
+  if (cols % (layout == Q4_LAYOUT_TILED ? 512 : g)) return Q4_ERR_SHAPE;
+  // the tiled layout stores whole 16-row tiles; per stored row both layouts
+  // hold cols/2 code bytes and cols/g scales (fp16 for INT4)
+  const size_t srows = layout == Q4_LAYOUT_TILED ? (size_t)((rows + 15) / 16) * 16 : (size_t)rows;
+  if (codes_bytes) *codes_bytes = srows * (size_t)cols / 2;
+  if (scales_bytes) *scales_bytes = srows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : 1);
   return Q4_OK;
 }
 
@@ -113,7 +118,7 @@ q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
   if (st != Q4_OK) return st;
   if (dst->fmt != Q4_NVFP4 && (dst->rows == 0 || dst->cols == 0)) return Q4_OK;
   return hip_status(q4::launch_quantize(
-      dst->fmt, static_cast<const uint16_t*>(src_bf16), ld, dst->rows, dst->cols,
+      dst->fmt, dst->layout, static_cast<const uint16_t*>(src_bf16), ld, dst->rows, dst->cols,
       static_cast<uint8_t*>(dst->codes), dst->scales, dst->global_scale, nv_global_in,
       as_stream(stream)));
 }
@@ -126,7 +131,7 @@ q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld,
   if (!dst) return Q4_ERR_NULL;
   if (ld < src->cols) return Q4_ERR_SHAPE;
   if (!aligned(dst, 16) || ld % (dst_dtype == 0 ? 8 : 4)) return Q4_ERR_ALIGN;
-  return hip_status(q4::launch_dequant(src->fmt, static_cast<const uint8_t*>(src->codes),
+  return hip_status(q4::launch_dequant(src->fmt, src->layout, static_cast<const uint8_t*>(src->codes),
                                        src->scales, src->global_scale, src->rows, src->cols, dst,
                                        dst_dtype, ld, as_stream(stream)));
 }
@@ -143,7 +148,7 @@ q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx
   if (st != Q4_OK) return st;
   st = check_out_bf16(y_bf16, B, W->rows, ldy);
   if (st != Q4_OK) return st;
-  return hip_status(q4::launch_gemv(W->fmt, static_cast<const uint8_t*>(W->codes), W->scales,
+  return hip_status(q4::launch_gemv(W->fmt, W->layout, static_cast<const uint8_t*>(W->codes), W->scales,
                                     W->global_scale, W->rows, W->cols,
                                     static_cast<const uint16_t*>(x_bf16), ldx, B,
                                     static_cast<uint16_t*>(y_bf16), ldy, as_stream(stream)));
@@ -173,10 +178,10 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
   if (st != Q4_OK) return st;
   if (A_q)
     return hip_status(q4::launch_gemm_w4a4(
-        static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,
+        A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,
         static_cast<const uint8_t*>(W->codes), static_cast<const uint8_t*>(W->scales), N, K,
         static_cast<uint16_t*>(C_bf16), ldc, as_stream(stream)));
-  return hip_status(q4::launch_gemm_w4a16(W->fmt, static_cast<const uint8_t*>(W->codes),
+  return hip_status(q4::launch_gemm_w4a16(W->fmt, W->layout, static_cast<const uint8_t*>(W->codes),
                                           W->scales, W->global_scale, N, K,
                                           static_cast<const uint16_t*>(A_bf16), lda, M,
                                           static_cast<uint16_t*>(C_bf16), ldc,
@@ -192,6 +197,7 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
   if (E < 0 || E > 65535 || N < 0 || T < 0 || P < 0 || P >= kMaxDim || T >= kMaxDim)
     return Q4_ERR_SHAPE;
   if (W->rows != (int64_t)E * N) return Q4_ERR_SHAPE;
+  if (W->layout == Q4_LAYOUT_TILED && N % 16) return Q4_ERR_SHAPE;  // experts own whole tiles
   const int64_t K = W->cols;
   if (K % 128) return Q4_ERR_SHAPE;
   if (E == 0 || N == 0 || P == 0) return Q4_OK;
@@ -200,10 +206,9 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
   if (!aligned(gather, 4) || !aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
   st = check_bf16(A_bf16, T, K, lda);
   if (st != Q4_OK) return st;
-  if (T > 0 && !A_bf16) return Q4_ERR_NULL;
   st = check_out_bf16(C_bf16, P, N, ldc);
   if (st != Q4_OK) return st;
-  return hip_status(q4::launch_grouped(W->fmt, static_cast<const uint16_t*>(A_bf16), lda, T,
+  return hip_status(q4::launch_grouped(W->fmt, W->layout, static_cast<const uint16_t*>(A_bf16), lda, T,
                                        gather, expert_offsets, E, P,
                                        static_cast<const uint8_t*>(W->codes), W->scales,
                                        W->global_scale, N, K, static_cast<uint16_t*>(C_bf16),

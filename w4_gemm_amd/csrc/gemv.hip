@@ -11,141 +11,286 @@
 //   * one v_mfma_f32_16x16x32_bf16 step multiplies a 16x32 tile of x (batch
 //     rows, zero beyond B) by a 32x16 tile of dequantized weights (16 output
 //     columns n).  Because a dot product does not care about the order of k,
-//     lane (n = l%16, g = l/16) loads the 16 bytes holding 32 consecutive
+//     lane (n = l%16, g = l/16) takes the 16 bytes holding 32 consecutive
 //     codes of row n -- exactly one MXFP4 block, two NVFP4 blocks, a quarter
-//     INT4 group -- and feeds them to four consecutive steps; the x lanes
-//     load the same 32 k for their batch row.  So 128 k (one super-chunk)
-//     cost one 16-byte weight load and one scale load per lane.
-//   * a wave owns RT tiles of 16 rows and reuses each x fragment across them.
-//   * the WAVES waves of a workgroup split K; their partial tiles are summed
-//     in LDS in a fixed order (deterministic) and written as bf16.
+//     INT4 group -- and feeds them to four consecutive steps; x is read for
+//     the same 32 k.  So 128 k (a super-chunk) cost one 16-byte code load per
+//     lane.  In the tiled layout (include/q4.h) that load is one contiguous
+//     kilobyte per wave; in the row-major layout it is 64 bytes of each of 16
+//     rows.
+//   * each wave owns one tile of 16 rows and walks the whole K in steps of
+//     4 super-chunks (512 k: 4 KB of codes and one 4- or 8-byte scale word
+//     per lane in the tiled layout).  The tiles of a workgroup's 4 waves are
+//     spread over the matrix (tile = wave * workgroups + workgroup).
+//   * x is staged in LDS once per step by the whole workgroup (BT rows,
+//     double-buffered) and shared by its waves.  The next step's x loads are
+//     issued first, then its code loads (non-temporal: the weights are
+//     streamed once), then the current step's math runs, and only then are
+//     the x values written to LDS -- so the wait for x never waits for the
+//     weights, and one step of weights is always in flight.  The per-step
+//     barrier keeps a workgroup's waves in lockstep, which measured faster
+//     than letting them drift.
+//   * the loop bodies issue their loads unconditionally (the tail steps are
+//     peeled, out-of-range x pieces are clamped and zeroed, surplus pieces go
+//     to a spare LDS slot) so the compiler's wait counts stay exact and the
+//     prefetched loads stay in flight across the math.
+//   * two accumulators (even / odd super-chunks) halve the dependent
+//     matrix-core chain; they are summed once at the end.
 #include "q4_launch.h"
+#include "q4_layout.h"
 #include "q4_mma.h"
 
 namespace q4 {
 namespace {
 
-template <int FMT, int RT, int WAVES>
-__global__ void __launch_bounds__(WAVES * 64)
+constexpr int kWaves = 4;            // waves (row tiles) per workgroup
+constexpr int kSCS = 4;              // super-chunks per step
+constexpr int kStepK = kSCS * 128;   // k per step
+
+// Registers of one step of one wave: the codes of its 4 super-chunks and the
+// raw scale words (row-major: one per super-chunk; tiled: one q group).
+template <int FMT, int LAYOUT>
+struct StepFrag {
+  static constexpr int NSW = LAYOUT == kLayoutRows ? kSCS : (FMT == 1 ? kSCS / 4 : kSCS / 2);
+  u32x4_t w[kSCS];
+  uint32_t sw[NSW];
+};
+
+// One wave streaming the codes and scales of one 16-row tile.
+template <int FMT, int LAYOUT>
+struct TileStream {
+  const uint8_t* wbase;  // this lane's code bytes of super-chunk 0
+  int64_t wstep;         // bytes between super-chunks
+  const uint8_t* sbase;  // this lane's scales
+  int nsc;               // super-chunks in K
+  int nq;                // q groups in K (tiled)
+
+  __device__ TileStream(const uint8_t* codes, const void* scales, int tile, int N, int K, int lane) {
+    const int col = lane & 15, grp = lane >> 4;
+    nsc = K >> 7;
+    nq = K >> 9;
+    if constexpr (LAYOUT == kLayoutRows) {
+      const int n = min(tile * 16 + col, N - 1);
+      wbase = codes + (int64_t)n * (K >> 1) + grp * 16;
+      wstep = 64;
+      sbase = reinterpret_cast<const uint8_t*>(scales) +
+              (int64_t)n * (K / FmtTraits<FMT>::G) * (FMT == 0 ? 2 : 1);
+      if constexpr (FMT == 1) sbase += grp;        // the lane's block in a super-chunk
+      if constexpr (FMT == 2) sbase += 2 * grp;    // the lane's two 16-blocks
+    } else {
+      const int64_t S = nsc, Q = nq;
+      wbase = codes + (int64_t)tile * S * 1024 + lane * 16;
+      wstep = 1024;
+      if constexpr (FMT == 0)
+        sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 16 + col) * 8;
+      else if constexpr (FMT == 1)
+        sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 64 + lane) * 4;
+      else
+        sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 64 + lane) * 8;
+    }
+  }
+
+  // Loads of step st (super-chunks past K are clamped to the last one).
+  __device__ __forceinline__ void load(StepFrag<FMT, LAYOUT>& f, int st) const {
+#pragma unroll
+    for (int c = 0; c < kSCS; ++c) {
+      const int sc = min(st * kSCS + c, nsc - 1);
+      f.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wbase + sc * wstep));
+      if constexpr (LAYOUT == kLayoutRows) {
+        if constexpr (FMT == 0) f.sw[c] = reinterpret_cast<const uint16_t*>(sbase)[sc];
+        else if constexpr (FMT == 1) f.sw[c] = sbase[sc * 4];
+        else f.sw[c] = *reinterpret_cast<const uint16_t*>(sbase + sc * 8);
+      }
+    }
+    if constexpr (LAYOUT == kLayoutTiled) {
+#pragma unroll
+      for (int h = 0; h < kSCS / 4; ++h) {  // the step's q groups
+        const int q = min((kSCS / 4) * st + h, nq - 1);
+        if constexpr (FMT == 1) {
+          f.sw[h] = reinterpret_cast<const uint32_t*>(sbase)[q * 64];
+        } else {
+          const int stride = FMT == 0 ? 16 * 8 : 64 * 8;  // bytes per q group
+          const uint2 v = *reinterpret_cast<const uint2*>(sbase + (int64_t)q * stride);
+          f.sw[2 * h] = v.x;
+          f.sw[2 * h + 1] = v.y;
+        }
+      }
+    }
+  }
+};
+
+// Scale bits of super-chunk c of a step for this lane: MXFP4 E8M0 byte;
+// NVFP4 the two E4M3 bytes of the lane's 32 k (first block low); INT4 fp16.
+template <int FMT, int LAYOUT>
+__device__ __forceinline__ uint32_t step_scale(const StepFrag<FMT, LAYOUT>& f, int c) {
+  if constexpr (LAYOUT == kLayoutRows) return f.sw[c];
+  else if constexpr (FMT == 1) return (f.sw[c >> 2] >> (8 * (c & 3))) & 0xFFu;
+  else return (f.sw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
+}
+
+// Dequantize one step and multiply it by x read from LDS at xrow (this
+// lane's batch row, already offset to the step and to the lane's 32 k).
+template <int FMT, int LAYOUT>
+__device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT>& f, const uint16_t* xrow,
+                                          bool xlane, float gs, f32x4_t& acc0, f32x4_t& acc1) {
+#pragma unroll
+  for (int c = 0; c < kSCS; ++c) {
+    const uint32_t sb = step_scale<FMT, LAYOUT>(f, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t xv = xlane ? *reinterpret_cast<const u32x4_t*>(xrow + c * 128 + 8 * i)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+      bf16x8_t wb;
+      if constexpr (FMT == 0) {
+        wb = dq8_int4(f.w[c][i], fp16_value(sb));
+      } else if constexpr (FMT == 1) {
+        wb = dq8_e2m1(f.w[c][i], e8m0_value(sb));
+      } else {
+        const uint32_t e = (i < 2) ? (sb & 0xFFu) : (sb >> 8);
+        wb = dq8_e2m1_mul(f.w[c][i], e4m3_value(e) * gs);
+      }
+      if (c & 1) acc1 = mma16x16x32(as_bf16x8(xv), wb, acc1);
+      else acc0 = mma16x16x32(as_bf16x8(xv), wb, acc0);
+    }
+  }
+}
+
+// lane l, register r of the accumulator holds (b = 4(l/16) + r, n = l%16)
+__device__ __forceinline__ void store_y(f32x4_t acc, int tile, int ntiles, int N, int B, int lane,
+                                        uint16_t* y, int64_t ldy) {
+  const int n = tile * 16 + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int b = 4 * (lane >> 4) + r;
+    if (b < B && n < N && tile < ntiles) y[(int64_t)b * ldy + n] = (uint16_t)f32_to_bf16_rne(acc[r]);
+  }
+}
+
+// x staged per step: [2][BT][kStepK + 8] bf16 (+ one spare 16-byte slot).
+template <int FMT, int LAYOUT, int BT>
+__global__ void __launch_bounds__(kWaves * 64)
 gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
             const float* __restrict__ gs_ptr, int N, int K,
             const uint16_t* __restrict__ x, int64_t ldx, int B,
             uint16_t* __restrict__ y, int64_t ldy) {
-  __shared__ f32x4_t red[WAVES][RT][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int n_base = blockIdx.x * (16 * RT);
-  const int nsc = K >> 7;
-  const int s_begin = (nsc * wave) / WAVES;
-  const int s_end = (nsc * (wave + 1)) / WAVES;
-  const int64_t row_bytes = K >> 1;
+  constexpr int XROW = kStepK + 8;
+  constexpr int XPIECES = BT * kStepK / 8;                  // 16-byte pieces per step
+  constexpr int XPER = (XPIECES + 64 * kWaves - 1) / (64 * kWaves);  // per thread
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_raw[];
+  auto xs = reinterpret_cast<uint16_t(*)[BT][XROW]>(xs_raw);
+  constexpr int W = kWaves;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int ntiles = (N + 15) >> 4;
+  const int tile = wave * gridDim.x + blockIdx.x;
+  const int nst = (K + kStepK - 1) / kStepK;
 
-  const uint8_t* wrow[RT];
-  int64_t srow[RT];
+  // Staging without branches: out-of-range pieces load a clamped address and
+  // are zeroed; surplus pieces go to the spare slot.  This keeps the
+  // compiler's count of outstanding loads exact.
+  auto load_x = [&](u32x4_t (&xr)[XPER], int st) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int n = min(n_base + 16 * rt + col, N - 1);  // clamped: tail lanes load a valid row
-    wrow[rt] = codes + (int64_t)n * row_bytes;
-    srow[rt] = (int64_t)n * (K / (FMT == 0 ? 128 : (FMT == 1 ? 32 : 16)));
-  }
-  const bool xlane = col < B;
-  const uint16_t* xrow = x + (int64_t)(xlane ? col : 0) * ldx;
+    for (int j = 0; j < XPER; ++j) {
+      const int p = min(tid + j * W * 64, XPIECES - 1);
+      const int b = p / (kStepK / 8);
+      const int k = st * kStepK + (p % (kStepK / 8)) * 8;
+      const bool ok = b < B && k < K;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(b, B - 1) * ldx +
+                                                          min(k, K - 8));
+      xr[j] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](const u32x4_t (&xr)[XPER], int buf) {
+#pragma unroll
+    for (int j = 0; j < XPER; ++j) {
+      const int p = tid + j * W * 64;
+      uint16_t* dst = p < XPIECES ? &xs[buf][p / (kStepK / 8)][(p % (kStepK / 8)) * 8]
+                                  : &xs_raw[2 * BT * XROW];
+      *reinterpret_cast<u32x4_t*>(dst) = xr[j];
+    }
+  };
+
+  const TileStream<FMT, LAYOUT> ts(codes, scales, min(tile, ntiles - 1), N, K, lane);
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
+  const bool xlane = col < BT;
+  const int xoff = (xlane ? col : 0) * XROW + grp * 32;
+  f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  f32x4_t acc[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int s = s_begin; s < s_end; ++s) {
-    const int k0 = (s << 7) + (grp << 5);
-    u32x4_t wq[RT];
-    uint32_t sraw[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      wq[rt] = *reinterpret_cast<const u32x4_t*>(wrow[rt] + (k0 >> 1));
-      if constexpr (FMT == 0)
-        sraw[rt] = reinterpret_cast<const uint16_t*>(scales)[srow[rt] + s];
-      else if constexpr (FMT == 1)
-        sraw[rt] = reinterpret_cast<const uint8_t*>(scales)[srow[rt] + (k0 >> 5)];
-      else
-        sraw[rt] = *reinterpret_cast<const uint16_t*>(
-            reinterpret_cast<const uint8_t*>(scales) + srow[rt] + (k0 >> 4));
-    }
-    u32x4_t xv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xv[i] = xlane ? *reinterpret_cast<const u32x4_t*>(xrow + k0 + 8 * i)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x8_t wb;
-        if constexpr (FMT == 0) {
-          wb = dq8_int4(wq[rt][i], fp16_value(sraw[rt]));
-        } else if constexpr (FMT == 1) {
-          wb = dq8_e2m1(wq[rt][i], e8m0_value(sraw[rt]));
-        } else {
-          const uint32_t sb = (i < 2) ? (sraw[rt] & 0xFFu) : (sraw[rt] >> 8);
-          wb = dq8_e2m1_mul(wq[rt][i], e4m3_value(sb) * gs);
-        }
-        acc[rt] = mma16x16x32(as_bf16x8(xv[i]), wb, acc[rt]);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) red[wave][rt][lane] = acc[rt];
+  // two buffers; the next step's x loads are issued before its code loads
+  // and written to LDS after the current step's math
+  StepFrag<FMT, LAYOUT> fa, fb;
+  u32x4_t xr[XPER];
+  load_x(xr, 0);
+  ts.load(fa, 0);
+  store_x(xr, 0);
   __syncthreads();
-  // lane l, register r of a tile holds (b = 4(l/16) + r, n = l%16)
-  for (int idx = threadIdx.x; idx < RT * 256; idx += WAVES * 64) {
-    const int rt = idx >> 8;
-    const int b = (idx >> 4) & 15;
-    const int nn = idx & 15;
-    const int src_lane = ((b >> 2) << 4) | nn;
-    float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][rt][src_lane][b & 3];
-    const int n = n_base + 16 * rt + nn;
-    if (b < B && n < N) y[(int64_t)b * ldy + n] = (uint16_t)f32_to_bf16_rne(v);
+  int st = 0;
+  for (; st + 2 < nst; st += 2) {
+    load_x(xr, st + 1);
+    ts.load(fb, st + 1);
+    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+    store_x(xr, (st + 1) & 1);
+    __syncthreads();
+    load_x(xr, st + 2);
+    ts.load(fa, st + 2);
+    step_math<FMT, LAYOUT>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+    store_x(xr, st & 1);
+    __syncthreads();
   }
+  if (st + 1 < nst) {  // two steps left
+    load_x(xr, st + 1);
+    ts.load(fb, st + 1);
+    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+    store_x(xr, (st + 1) & 1);
+    __syncthreads();
+    step_math<FMT, LAYOUT>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+  } else {             // one step left
+    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+  }
+
+  store_y(acc0 + acc1, tile, ntiles, N, B, lane, y, ldy);
 }
 
-template <int FMT, int RT, int WAVES>
+template <int FMT, int LAYOUT, int BT>
 hipError_t run(const uint8_t* codes, const void* scales, const float* gs, int64_t N, int64_t K,
                const uint16_t* x, int64_t ldx, int64_t B, uint16_t* y, int64_t ldy,
                hipStream_t stream) {
-  const unsigned grid = (unsigned)((N + 16 * RT - 1) / (16 * RT));
-  gemv_kernel<FMT, RT, WAVES><<<grid, WAVES * 64, 0, stream>>>(
+  const int64_t ntiles = (N + 15) / 16;
+  const unsigned grid = (unsigned)((ntiles + kWaves - 1) / kWaves);
+  const size_t lds = (2ull * BT * (kStepK + 8) + 8) * sizeof(uint16_t);  // + spare slot
+  gemv_kernel<FMT, LAYOUT, BT><<<grid, kWaves * 64, lds, stream>>>(
       codes, scales, gs, (int)N, (int)K, x, ldx, (int)B, y, ldy);
   return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t dispatch(const uint8_t* codes, const void* scales, const float* gs, int64_t N,
+template <int FMT, int LAYOUT>
+hipError_t by_batch(const uint8_t* codes, const void* scales, const float* gs, int64_t N,
                     int64_t K, const uint16_t* x, int64_t ldx, int64_t B, uint16_t* y,
                     int64_t ldy, hipStream_t stream) {
-  // Enough workgroups to cover 256 CUs several times, K split 8 ways when
-  // there are at least 8 super-chunks of 128.
-  if (K >= 1024) {
-    if (N >= 16384) return run<FMT, 4, 8>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
-    if (N >= 4096) return run<FMT, 2, 8>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
-    return run<FMT, 1, 8>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
-  }
-  return run<FMT, 1, 4>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  // x rows held in LDS: 1, 4 or 16 (the matrix core always computes 16)
+  if (B == 1) return run<FMT, LAYOUT, 1>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  if (B <= 4) return run<FMT, LAYOUT, 4>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  return run<FMT, LAYOUT, 16>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+}
+
+template <int FMT>
+hipError_t dispatch(int layout, const uint8_t* codes, const void* scales, const float* gs,
+                    int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t B, uint16_t* y,
+                    int64_t ldy, hipStream_t stream) {
+  if (layout == kLayoutTiled)
+    return by_batch<FMT, kLayoutTiled>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  return by_batch<FMT, kLayoutRows>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int fmt, const uint8_t* codes, const void* scales, const float* gs,
-                       int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t B,
-                       uint16_t* y, int64_t ldy, hipStream_t stream) {
+hipError_t launch_gemv(int fmt, int layout, const uint8_t* codes, const void* scales,
+                       const float* gs, int64_t N, int64_t K, const uint16_t* x, int64_t ldx,
+                       int64_t B, uint16_t* y, int64_t ldy, hipStream_t stream) {
   if (N == 0 || B == 0) return hipSuccess;
-  if (fmt == 0) return dispatch<0>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
-  if (fmt == 1) return dispatch<1>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
-  return dispatch<2>(codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  if (fmt == 0) return dispatch<0>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  if (fmt == 1) return dispatch<1>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  return dispatch<2>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
 }
 
 }  // namespace q4

@@ -9,34 +9,35 @@
 namespace q4 {
 
 // Quantize bf16 src [rows][ld] into codes/scales (fmt 0 INT4 g128,
-// 1 MXFP4, 2 NVFP4).  NVFP4: gs receives the global scale; gs_in, when not
-// null, supplies it instead of the tensor-absmax pass.
-hipError_t launch_quantize(int fmt, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols,
-                           uint8_t* codes, void* scales, float* gs, const float* gs_in,
-                           hipStream_t stream);
+// 1 MXFP4, 2 NVFP4; layout 0 row-major, 1 tiled).  NVFP4: gs receives the
+// global scale; gs_in, when not null, supplies it instead of the
+// tensor-absmax pass.
+hipError_t launch_quantize(int fmt, int layout, const uint16_t* src, int64_t ld, int64_t rows,
+                           int64_t cols, uint8_t* codes, void* scales, float* gs,
+                           const float* gs_in, hipStream_t stream);
 
-// Dequantize into dst [rows][ld], dst_dtype 0 bf16 / 1 fp32.
-hipError_t launch_dequant(int fmt, const uint8_t* codes, const void* scales, const float* gs,
-                          int64_t rows, int64_t cols, void* dst, int dst_dtype, int64_t ld,
-                          hipStream_t stream);
+// Dequantize into row-major dst [rows][ld], dst_dtype 0 bf16 / 1 fp32.
+hipError_t launch_dequant(int fmt, int layout, const uint8_t* codes, const void* scales,
+                          const float* gs, int64_t rows, int64_t cols, void* dst, int dst_dtype,
+                          int64_t ld, hipStream_t stream);
 
-// W4A16 GEMV, 1 <= B <= 16, K % 128 == 0.
-hipError_t launch_gemv(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+// W4A16 GEMV, 1 <= B <= 16, K % 128 == 0 (row-major) / 512 (tiled).
+hipError_t launch_gemv(int fmt, int layout, const uint8_t* codes, const void* scales, const float* gs,
                        int64_t N, int64_t K, const uint16_t* x, int64_t ldx, int64_t B,
                        uint16_t* y, int64_t ldy, hipStream_t stream);
 
 // W4A16 GEMM C [M][ldc] = A [M][lda] . W'^T, K % 128 == 0.
-hipError_t launch_gemm_w4a16(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+hipError_t launch_gemm_w4a16(int fmt, int layout, const uint8_t* codes, const void* scales, const float* gs,
                              int64_t N, int64_t K, const uint16_t* A, int64_t lda, int64_t M,
                              uint16_t* C, int64_t ldc, hipStream_t stream);
 
 // W4A4 MXFP4 GEMM C [M][ldc] = A' . W'^T, both MXFP4, K % 128 == 0.
-hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+hipError_t launch_gemm_w4a4(int a_layout, int w_layout, const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
                             uint16_t* C, int64_t ldc, hipStream_t stream);
 
 // Grouped expert GEMM (W4A16), see q4_grouped_gemm.
-hipError_t launch_grouped(int fmt, const uint16_t* A, int64_t lda, int64_t T,
+hipError_t launch_grouped(int fmt, int layout, const uint16_t* A, int64_t lda, int64_t T,
                           const int32_t* gather, const int32_t* offsets, int32_t E, int64_t P,
                           const uint8_t* codes, const void* scales, const float* gs, int64_t N,
                           int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);

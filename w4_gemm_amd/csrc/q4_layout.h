@@ -1,0 +1,60 @@
+// q4_layout.h -- byte offsets of codes and scales in the two layouts of a
+// quantized tensor (row-major and 16x128 tiled; the layouts are defined in
+// include/q4.h).  Shared by the quantizer, the dequantizer and the matmul
+// kernels so every kernel addresses a tensor the same way.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+constexpr int kLayoutRows = 0;
+constexpr int kLayoutTiled = 1;
+
+template <int FMT>
+struct FmtTraits {
+  static constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);  // block size along K
+};
+
+// Byte offset of the 4 code bytes holding elements k0..k0+7 (k0 % 8 == 0)
+// of row r.  K = columns.
+template <int LAYOUT>
+__host__ __device__ __forceinline__ int64_t code_off8(int64_t r, int64_t k0, int64_t K) {
+  if constexpr (LAYOUT == kLayoutRows) {
+    return r * (K >> 1) + (k0 >> 1);
+  } else {
+    const int64_t S = K >> 7;
+    const int64_t t = r >> 4, n = r & 15, s = k0 >> 7, g = (k0 >> 5) & 3, piece = (k0 >> 3) & 3;
+    return ((t * S + s) << 10) + ((g * 16 + n) << 4) + (piece << 2);
+  }
+}
+
+// Offset (in scale elements: fp16 for INT4, bytes otherwise) of the scale of
+// the block holding element k of row r.
+template <int FMT, int LAYOUT>
+__host__ __device__ __forceinline__ int64_t scale_off(int64_t r, int64_t k, int64_t K) {
+  if constexpr (LAYOUT == kLayoutRows) {
+    return r * (K / FmtTraits<FMT>::G) + k / FmtTraits<FMT>::G;
+  } else {
+    const int64_t Q = K >> 9;
+    const int64_t t = r >> 4, n = r & 15, s = k >> 7, q = s >> 2, i = s & 3;
+    if constexpr (FMT == 0) {
+      return (((t * Q + q) << 4) + n) * 4 + i;
+    } else {
+      const int64_t g = (k >> 5) & 3;
+      const int64_t l = g * 16 + n;
+      if constexpr (FMT == 1) return (((t * Q + q) << 6) + l) * 4 + i;
+      const int64_t h = (k >> 4) & 1;
+      return (((t * Q + q) << 6) + l) * 8 + 2 * i + h;
+    }
+  }
+}
+
+// Rows of storage (the tiled layout pads the last tile to 16 rows).
+template <int LAYOUT>
+__host__ __device__ __forceinline__ int64_t stored_rows(int64_t rows) {
+  return LAYOUT == kLayoutRows ? rows : ((rows + 15) >> 4) << 4;
+}
+
+}  // namespace q4

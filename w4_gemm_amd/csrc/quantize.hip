@@ -14,12 +14,15 @@
 //              (same file, nvfp4)
 //
 // Launch shape: one lane per 8 consecutive values of a row (one 16-byte
-// load, one 4-byte store of packed nibbles).  A block of g values is g/8
-// adjacent lanes (16 for INT4, 4 for MXFP4, 2 for NVFP4); its absmax is a
-// butterfly max over those lanes.  Every lane of a wave runs the same number
-// of iterations so the cross-lane steps see the whole group.
+// load, one 4-byte store of packed nibbles at the position the layout
+// gives).  A block of g values is g/8 adjacent lanes (16 for INT4, 4 for
+// MXFP4, 2 for NVFP4); its absmax is a butterfly max over those lanes.
+// Every lane of a wave runs the same number of iterations so the cross-lane
+// steps see the whole group.  In the tiled layout the padding rows of the
+// last tile are quantized as zeros.
 #include "q4_device.h"
 #include "q4_launch.h"
+#include "q4_layout.h"
 
 #pragma clang fp contract(off)
 
@@ -76,16 +79,15 @@ __device__ __forceinline__ float absmax8(const Chunk8& c) {
 // global scale (gs_is_amax = 0) or the raw bits of the tensor absmax
 // (gs_is_amax = 1).  gs_out (NVFP4, may equal gs_src only when
 // gs_is_amax = 0) receives gs from the first lane.
-template <int FMT>
+template <int FMT, int LAYOUT>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
                 uint8_t* __restrict__ codes, void* __restrict__ scales,
                 const float* gs_src, int gs_is_amax, float* gs_out) {
-  constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);
+  constexpr int G = FmtTraits<FMT>::G;
   constexpr int LANES = G / 8;
   const int64_t cpr = cols >> 3;  // chunks of 8 per row
-  const int64_t total = rows * cpr;
-  const int64_t nblk = cols / G;
+  const int64_t total = stored_rows<LAYOUT>(rows) * cpr;
 
   float gs = 0.0f;
   if constexpr (FMT == 2) {
@@ -103,7 +105,8 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
     const bool valid = c < total;
     const int64_t r = valid ? c / cpr : 0;
     const int64_t k0 = valid ? (c - r * cpr) * 8 : 0;
-    Chunk8 x = load8(src + r * ld + k0, valid);
+    const bool in_src = valid && r < rows;  // tiled padding rows read as zeros
+    Chunk8 x = load8(src + (in_src ? r * ld + k0 : 0), in_src);
     const float amax = group_max<LANES>(absmax8(x));
 
     uint32_t packed = 0;
@@ -121,12 +124,12 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
         packed |= ((uint32_t)q & 0xFu) << (4 * j);
       }
       if (valid && (k0 % G) == 0)
-        reinterpret_cast<uint16_t*>(scales)[r * nblk + k0 / G] = (uint16_t)sbits;
+        reinterpret_cast<uint16_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint16_t)sbits;
     } else if constexpr (FMT == 1) {
       const uint32_t e = mx_e8m0(amax);
       packed = e2m1_pack8(x, e8m0_value(e));
       if (valid && (k0 % G) == 0)
-        reinterpret_cast<uint8_t*>(scales)[r * nblk + k0 / G] = (uint8_t)e;
+        reinterpret_cast<uint8_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint8_t)e;
     } else {
       const float t = fminf((amax / 6.0f) / gs, 448.0f);
       const uint32_t sc = e4m3_encode(t);
@@ -141,9 +144,9 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
         packed = e2m1_pack8(y, 1.0f);
       }
       if (valid && (k0 % G) == 0)
-        reinterpret_cast<uint8_t*>(scales)[r * nblk + k0 / G] = (uint8_t)sc;
+        reinterpret_cast<uint8_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint8_t)sc;
     }
-    if (valid) *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + (k0 >> 1)) = packed;
+    if (valid) *reinterpret_cast<uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols)) = packed;
   }
 }
 
@@ -182,22 +185,20 @@ __global__ void finalize_gs_kernel(float* gs) {
 }
 
 // Dequantize: one lane per 8 values; OUT 0 = bf16, 1 = fp32.
-template <int FMT, int OUT>
+template <int FMT, int OUT, int LAYOUT>
 __global__ void __launch_bounds__(kThreads)
 dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
                const float* gs_ptr, int64_t rows, int64_t cols, void* __restrict__ dst,
                int64_t ld) {
-  constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
-  const int64_t nblk = cols / G;
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
   for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
        c += (int64_t)gridDim.x * kThreads) {
     const int64_t r = c / cpr;
     const int64_t k0 = (c - r * cpr) * 8;
-    const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + (k0 >> 1));
-    const int64_t si = r * nblk + k0 / G;
+    const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols));
+    const int64_t si = scale_off<FMT, LAYOUT>(r, k0, cols);
     float v[8];
     if constexpr (FMT == 0) {
       const float s = fp16_value(reinterpret_cast<const uint16_t*>(scales)[si]);
@@ -237,21 +238,20 @@ unsigned grid_for(int64_t chunks) {
   return (unsigned)b;
 }
 
-}  // namespace
-
-hipError_t launch_quantize(int fmt, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols,
+template <int LAYOUT>
+hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols,
                            uint8_t* codes, void* scales, float* gs, const float* gs_in,
                            hipStream_t stream) {
-  const int64_t chunks = rows * (cols >> 3);
+  const int64_t chunks = stored_rows<LAYOUT>(rows) * (cols >> 3);
   const unsigned grid = grid_for(chunks);
   if (fmt == 0) {
-    if (chunks) quantize_kernel<0><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+    if (chunks) quantize_kernel<0, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
   } else if (fmt == 1) {
-    if (chunks) quantize_kernel<1><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+    if (chunks) quantize_kernel<1, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
   } else {
     if (gs_in) {
       if (chunks) {
-        quantize_kernel<2><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs_in, 0, gs);
+        quantize_kernel<2, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs_in, 0, gs);
       } else {
         // nothing to quantize: still record the caller's gs
         hipError_t e = hipMemcpyAsync(gs, gs_in, sizeof(float), hipMemcpyDeviceToDevice, stream);
@@ -261,9 +261,13 @@ hipError_t launch_quantize(int fmt, const uint16_t* src, int64_t ld, int64_t row
       uint32_t* amax = reinterpret_cast<uint32_t*>(gs);
       set_word_kernel<<<1, 1, 0, stream>>>(amax, 0u);
       if (chunks) {
-        const unsigned agrid = (unsigned)(grid < 2048 ? grid : 2048);
-        absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
-        quantize_kernel<2><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs, 1, nullptr);
+        const int64_t src_chunks = rows * (cols >> 3);
+        if (src_chunks) {
+          const unsigned sgrid = grid_for(src_chunks);
+          const unsigned agrid = sgrid < 2048 ? sgrid : 2048;
+          absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
+        }
+        quantize_kernel<2, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs, 1, nullptr);
       }
       finalize_gs_kernel<<<1, 1, 0, stream>>>(gs);
     }
@@ -271,13 +275,14 @@ hipError_t launch_quantize(int fmt, const uint16_t* src, int64_t ld, int64_t row
   return hipGetLastError();
 }
 
-hipError_t launch_dequant(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+template <int LAYOUT>
+hipError_t dequant_layout(int fmt, const uint8_t* codes, const void* scales, const float* gs,
                           int64_t rows, int64_t cols, void* dst, int dst_dtype, int64_t ld,
                           hipStream_t stream) {
   const int64_t chunks = rows * (cols >> 3);
   if (!chunks) return hipSuccess;
   const unsigned grid = grid_for(chunks);
-#define Q4_DQ(F, O) dequant_kernel<F, O><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
+#define Q4_DQ(F, O) dequant_kernel<F, O, LAYOUT><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
   if (dst_dtype == 0) {
     if (fmt == 0) Q4_DQ(0, 0); else if (fmt == 1) Q4_DQ(1, 0); else Q4_DQ(2, 0);
   } else {
@@ -285,6 +290,24 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const void* scales, con
   }
 #undef Q4_DQ
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int fmt, int layout, const uint16_t* src, int64_t ld, int64_t rows,
+                           int64_t cols, uint8_t* codes, void* scales, float* gs,
+                           const float* gs_in, hipStream_t stream) {
+  if (layout == kLayoutTiled)
+    return quantize_layout<kLayoutTiled>(fmt, src, ld, rows, cols, codes, scales, gs, gs_in, stream);
+  return quantize_layout<kLayoutRows>(fmt, src, ld, rows, cols, codes, scales, gs, gs_in, stream);
+}
+
+hipError_t launch_dequant(int fmt, int layout, const uint8_t* codes, const void* scales,
+                          const float* gs, int64_t rows, int64_t cols, void* dst, int dst_dtype,
+                          int64_t ld, hipStream_t stream) {
+  if (layout == kLayoutTiled)
+    return dequant_layout<kLayoutTiled>(fmt, codes, scales, gs, rows, cols, dst, dst_dtype, ld, stream);
+  return dequant_layout<kLayoutRows>(fmt, codes, scales, gs, rows, cols, dst, dst_dtype, ld, stream);
 }
 
 }  // namespace q4
