@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="headline workload only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of extra workloads to run")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                   help="also run a plain device copy of MB megabytes three times (the reference "
+                        "kernel for scaling HBM byte counters); prints nothing extra")
     return p.parse_args()
 
 
@@ -122,6 +125,15 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     q4.lib()  # fails loudly if the HIP library is missing
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy * 1000 * 1000
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- headline
     log("generating the MXFP4 decode workload (28672 x 8192)")
@@ -251,7 +263,7 @@ def _kernel_sha(name):
     import hashlib
     base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "w4_gemm_amd", "csrc")
     h = hashlib.sha256()
-    for f in (name, "q4_mma.h", "q4_device.h"):
+    for f in (name, "q4_mma.h", "q4_device.h", "q4_layout.h"):
         h.update(open(os.path.join(base, f), "rb").read())
     return h.hexdigest()[:16]
 
