@@ -300,6 +300,8 @@ hipError_t launch_gemm_w4a4(int a_layout, int w_layout, const uint8_t* a_codes,
                             const uint8_t* w_scales, int64_t N, int64_t K, uint16_t* C,
                             int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (a_layout == kLayoutTiled && w_layout == kLayoutTiled)
+    return launch_gemm_w4a4_tiled(a_codes, a_scales, M, w_codes, w_scales, N, K, C, ldc, stream);
   const dim3 grid((unsigned)((N + WAVES * 16 * NT - 1) / (WAVES * 16 * NT)),
                   (unsigned)((M + 16 * MT - 1) / (16 * MT)));
 #define Q4_W4A4(AL, WL) w4a4_kernel<AL, WL><<<grid, WAVES * 64, 0, stream>>>(a_codes, a_scales, (int)M, w_codes, w_scales, (int)N, (int)K, C, ldc)

@@ -1,0 +1,236 @@
+// gemm_w4a4.hip -- W4A4 MXFP4 GEMM for operands in the tiled layout:
+// C[m][n] = sum_k a'[m][k] w'[n][k], both operands MXFP4 (E2M1 codes, one
+// E8M0 scale per 32 along K), fp32 accumulation, bf16 output.
+//
+// The W4A4 scheme quantizes the activations to FP4 as well and multiplies
+// on FP4 matrix cores directly ("Low-bit inference for very large MoE",
+// table "Kernels on different hardware", row W4A4).  On gfx950 that is
+// v_mfma_scale_f32_16x16x128_f8f6f4: lane l supplies the 32 codes of row
+// l%16, k in [32(l/16), +32) -- one MXFP4 block -- and that block's E8M0,
+// i.e. exactly lane l's 16 bytes of a 1 KB tile of the tiled layout
+// (include/q4.h) and byte 4l+i of its scale group.
+//
+// Work decomposition:
+//   * a workgroup of 8 waves computes a 256 x 256 block of C; wave (wm, wn),
+//     wm in 0..1, wn in 0..3, owns 128 x 64 = 8 x 4 matrix-core tiles (128
+//     fp32 accumulators per lane).  The scaled MFMA has no form whose result
+//     register is its accumulator input, so the accumulators must leave room
+//     for a free destination: 256 per lane would fill the accumulator file.
+//   * K advances in stages of one super-chunk (128 k).  A stage needs 16
+//     A tiles and 16 W tiles (32 KB); they are copied verbatim into LDS by
+//     direct global->LDS loads (global_load_lds_dwordx4: one 1 KB tile per
+//     wave instruction, no registers; 4 per wave), two stages ahead, into
+//     three buffers.  Scales are copied per group of four stages (16 x 256 B for
+//     each operand) into two buffers.  Every fragment read from LDS is one
+//     contiguous kilobyte (conflict-free).
+//   * one barrier per stage: each wave first waits (explicit vmcnt) for its
+//     own copies of the current stage, the barrier then makes every wave's
+//     copies visible and also guarantees that the buffer the next copies
+//     overwrite is no longer read.  The stage loop is unrolled by four so
+//     each wait count is a constant.
+//   * workgroups are ordered so that the 32 running on one XCD cover a
+//     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
+#include "q4_launch.h"
+#include "q4_layout.h"
+#include "q4_mma.h"
+
+namespace q4 {
+namespace {
+
+constexpr int kBM = 16;          // A tiles (of 16 rows) per workgroup
+constexpr int kBN = 16;          // W tiles per workgroup
+constexpr int kTiles = kBM + kBN;
+constexpr int kWaves = 8;
+constexpr int kCopies = kTiles / kWaves;  // code tiles each wave copies per stage
+constexpr int kCodeBufs = 3;
+constexpr size_t kSmemBytes = kCodeBufs * kTiles * 1024 + 2 * kTiles * 256;  // 112 KB
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
+  // each lane copies 16 bytes from src to lds_base + 16 * lane
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base,
+                                   16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS accesses without waiting for the
+// outstanding global->LDS copies (the wave's own copies are waited for
+// explicitly, by count, before it).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(kWaves * 64)
+w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+                  int M, const uint8_t* __restrict__ w_codes,
+                  const uint8_t* __restrict__ w_scales, int N, int K,
+                  uint16_t* __restrict__ C, int64_t ldc) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t (*cbuf)[kTiles][1024] = reinterpret_cast<uint8_t (*)[kTiles][1024]>(smem);
+  uint8_t (*sbuf)[kTiles][256] =
+      reinterpret_cast<uint8_t (*)[kTiles][256]>(smem + kCodeBufs * kTiles * 1024);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int S = K >> 7, Q = K >> 9;
+  const int RTA = (M + 15) >> 4, RTW = (N + 15) >> 4;
+
+  // workgroup -> 256 x 256 block of C: XCD-major, then groups of 4 block rows
+  const int TM = (M + 255) >> 8, TN = (N + 255) >> 8, T = TM * TN;
+  const int b = blockIdx.x;
+  const int lin = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int GM = 4, gsz = GM * TN;
+  const int first_m = (lin / gsz) * GM;
+  const int gm = min(TM - first_m, GM);
+  const int bm = first_m + (lin % gsz) % gm;
+  const int bn = (lin % gsz) / gm;
+
+  // the tiles this wave copies each stage: WG tiles kCopies*wave + k
+  // (0..15 are A row tiles bm*16 + i, 16..31 are W row tiles bn*16 + i)
+  // (wave-uniform bases; the lane offset is added at each copy)
+  const uint8_t* csrc[kCopies];
+#pragma unroll
+  for (int k = 0; k < kCopies; ++k) {
+    const int ti = kCopies * wave + k;
+    csrc[k] = ti < kBM ? a_codes + (int64_t)min(bm * kBM + ti, RTA - 1) * S * 1024
+                       : w_codes + (int64_t)min(bn * kBN + ti - kBM, RTW - 1) * S * 1024;
+  }
+  // the scale copy of this wave: the 256-byte groups of tiles 4*wave + 0..3
+  // (lane -> tile 4*wave + lane/16, bytes 16*(lane%16) ..)
+  const int sti = 4 * wave + (lane >> 4);
+  const uint8_t* ssrc = (sti < kBM ? a_scales + (int64_t)min(bm * kBM + sti, RTA - 1) * Q * 256
+                                   : w_scales + (int64_t)min(bn * kBN + sti - kBM, RTW - 1) * Q * 256) +
+                        (lane & 15) * 16;
+
+  // copy group t: the codes of stage t (kCopies per wave), plus the scales
+  // of group t/4 when t % 4 == 0 (1 per wave).  Past the end the last stage /
+  // group is copied again (into free buffers) so every group issues the same
+  // number of copies.
+  auto issue_codes = [&](int t) {
+    const int st = min(t, S - 1);
+    uint8_t(*dst)[1024] = cbuf[t % kCodeBufs];
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k)
+      copy16_to_lds(csrc[k] + (int64_t)st * 1024 + lane * 16, dst[kCopies * wave + k]);
+  };
+  auto issue_scales = [&](int t) {
+    const int q = min(t >> 2, Q - 1);
+    copy16_to_lds(ssrc + (int64_t)q * 256, sbuf[(t >> 2) & 1][4 * wave]);
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t sa[8], sw[4];
+
+  // math of stage s (j = s % 4 known at compile time)
+  auto compute = [&](int s, int j) {
+    const uint8_t(*cb)[1024] = cbuf[s % kCodeBufs];
+    if (j == 0) {
+      const uint8_t(*sb)[256] = sbuf[(s >> 2) & 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        sa[i] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + i][lane * 4]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        sw[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
+    }
+    i32x8_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t va = *reinterpret_cast<const u32x4_t*>(&cb[wm * 8 + i][lane * 16]);
+      a[i] = i32x8_t{(int)va[0], (int)va[1], (int)va[2], (int)va[3], 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + jj][lane * 16]);
+      const i32x8_t w = i32x8_t{(int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3], 0, 0, 0, 0};
+      const int ew = (sw[jj] >> (8 * j)) & 0xFF;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ea = (sa[i] >> (8 * j)) & 0xFF;
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], w, acc[i][jj], 4, 4, 0,
+                                                                      ea, 0, ew);
+      }
+    }
+  };
+
+  // prologue: groups 0 (codes + scales) and 1 (codes)
+  issue_codes(0);
+  issue_scales(0);
+  issue_codes(1);
+
+  // iteration s: wait for group s (group s+1 may stay in flight), barrier,
+  // issue group s+2 into the buffers of stage s-1, compute stage s.
+  // Copies in group s+1: kCopies, plus 1 when (s+1) % 4 == 0.
+  // The tiled layout has K % 512 == 0, so S is a multiple of 4.
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    // j = 0
+    wait_vmcnt<kCopies>();
+    stage_barrier();
+    issue_codes(s0 + 2);
+    compute(s0, 0);
+    // j = 1
+    wait_vmcnt<kCopies>();
+    stage_barrier();
+    issue_codes(s0 + 3);
+    compute(s0 + 1, 1);
+    // j = 2: group s0+4 starts a new scale group
+    wait_vmcnt<kCopies>();
+    stage_barrier();
+    issue_codes(s0 + 4);
+    issue_scales(s0 + 4);
+    compute(s0 + 2, 2);
+    // j = 3: group s0+4 (outstanding) also holds its scale copy
+    wait_vmcnt<kCopies + 1>();
+    stage_barrier();
+    issue_codes(s0 + 5);
+    compute(s0 + 3, 3);
+  }
+  wait_vmcnt<0>();
+
+  // lane l, register r of tile (i, jj) holds row 4(l/16) + r, column l%16
+  const int row0 = bm * 256 + wm * 128;
+  const int col0 = bn * 256 + wn * 64 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int n = col0 + jj * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = row0 + i * 16 + 4 * (lane >> 4) + r;
+        if (m < M && n < N) C[(int64_t)m * ldc + n] = (uint16_t)f32_to_bf16_rne(acc[i][jj][r]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                  int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&w4a4_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kSmemBytes);
+  if (attr != hipSuccess) return attr;
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  w4a4_tiled_kernel<<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(a_codes, a_scales, (int)M, w_codes,
+                                                              w_scales, (int)N, (int)K, C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -36,6 +36,12 @@ hipError_t launch_gemm_w4a4(int a_layout, int w_layout, const uint8_t* a_codes, 
                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
                             uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// W4A4 with both operands in the tiled layout (K % 512 == 0): the
+// LDS-staged kernel of gemm_w4a4.hip.
+hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                  int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
+
 // Grouped expert GEMM (W4A16), see q4_grouped_gemm.
 hipError_t launch_grouped(int fmt, int layout, const uint16_t* A, int64_t lda, int64_t T,
                           const int32_t* gather, const int32_t* offsets, int32_t E, int64_t P,
