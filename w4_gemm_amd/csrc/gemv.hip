@@ -65,6 +65,7 @@ struct TileStream {
   int nsc;               // super-chunks in K
   int nq;                // q groups in K (tiled)
 
+  TileStream() = default;
   __device__ TileStream(const uint8_t* codes, const void* scales, int tile, int N, int K, int lane) {
     const int col = lane & 15, grp = lane >> 4;
     nsc = K >> 7;
@@ -128,29 +129,34 @@ __device__ __forceinline__ uint32_t step_scale(const StepFrag<FMT, LAYOUT>& f, i
   else return (f.sw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
 }
 
-// Dequantize one step and multiply it by x read from LDS at xrow (this
-// lane's batch row, already offset to the step and to the lane's 32 k).
-template <int FMT, int LAYOUT>
-__device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT>& f, const uint16_t* xrow,
-                                          bool xlane, float gs, f32x4_t& acc0, f32x4_t& acc1) {
+// Dequantize one step of TPW tiles and multiply them by x read from LDS at
+// xrow (this lane's batch row, already offset to the step and to the lane's
+// 32 k); each x fragment feeds every tile.
+template <int FMT, int LAYOUT, int TPW>
+__device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW], const uint16_t* xrow,
+                                          bool xlane, float gs, f32x4_t (&acc)[TPW][2]) {
 #pragma unroll
   for (int c = 0; c < kSCS; ++c) {
-    const uint32_t sb = step_scale<FMT, LAYOUT>(f, c);
+    uint32_t sb[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) sb[t] = step_scale<FMT, LAYOUT>(f[t], c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4_t xv = xlane ? *reinterpret_cast<const u32x4_t*>(xrow + c * 128 + 8 * i)
                                : u32x4_t{0u, 0u, 0u, 0u};
-      bf16x8_t wb;
-      if constexpr (FMT == 0) {
-        wb = dq8_int4(f.w[c][i], fp16_value(sb));
-      } else if constexpr (FMT == 1) {
-        wb = dq8_e2m1(f.w[c][i], e8m0_value(sb));
-      } else {
-        const uint32_t e = (i < 2) ? (sb & 0xFFu) : (sb >> 8);
-        wb = dq8_e2m1_mul(f.w[c][i], e4m3_value(e) * gs);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        bf16x8_t wb;
+        if constexpr (FMT == 0) {
+          wb = dq8_int4(f[t].w[c][i], fp16_value(sb[t]));
+        } else if constexpr (FMT == 1) {
+          wb = dq8_e2m1(f[t].w[c][i], e8m0_value(sb[t]));
+        } else {
+          const uint32_t e = (i < 2) ? (sb[t] & 0xFFu) : (sb[t] >> 8);
+          wb = dq8_e2m1_mul(f[t].w[c][i], e4m3_value(e) * gs);
+        }
+        acc[t][c & 1] = mma16x16x32(as_bf16x8(xv), wb, acc[t][c & 1]);
       }
-      if (c & 1) acc1 = mma16x16x32(as_bf16x8(xv), wb, acc1);
-      else acc0 = mma16x16x32(as_bf16x8(xv), wb, acc0);
     }
   }
 }
@@ -167,7 +173,8 @@ __device__ __forceinline__ void store_y(f32x4_t acc, int tile, int ntiles, int N
 }
 
 // x staged per step: [2][BT][kStepK + 8] bf16 (+ one spare 16-byte slot).
-template <int FMT, int LAYOUT, int BT>
+// Each wave owns TPW adjacent row tiles.
+template <int FMT, int LAYOUT, int BT, int TPW>
 __global__ void __launch_bounds__(kWaves * 64)
 gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
             const float* __restrict__ gs_ptr, int N, int K,
@@ -182,83 +189,102 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int ntiles = (N + 15) >> 4;
-  const int tile = wave * gridDim.x + blockIdx.x;
+  const int tile = (wave * gridDim.x + blockIdx.x) * TPW;  // first of the wave's tiles
   const int nst = (K + kStepK - 1) / kStepK;
 
   // Staging without branches: out-of-range pieces load a clamped address and
-  // are zeroed; surplus pieces go to the spare slot.  This keeps the
-  // compiler's count of outstanding loads exact.
+  // are zeroed when written to LDS (not at the load: using a loaded value
+  // right away would make the wave wait for it); surplus pieces go to the
+  // spare slot.  This keeps the compiler's count of outstanding loads exact.
+  auto piece = [&](int j) { return min(tid + j * W * 64, XPIECES - 1); };
   auto load_x = [&](u32x4_t (&xr)[XPER], int st) {
 #pragma unroll
     for (int j = 0; j < XPER; ++j) {
-      const int p = min(tid + j * W * 64, XPIECES - 1);
+      const int p = piece(j);
       const int b = p / (kStepK / 8);
       const int k = st * kStepK + (p % (kStepK / 8)) * 8;
-      const bool ok = b < B && k < K;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(b, B - 1) * ldx +
-                                                          min(k, K - 8));
-      xr[j] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+      xr[j] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(b, B - 1) * ldx + min(k, K - 8));
     }
   };
-  auto store_x = [&](const u32x4_t (&xr)[XPER], int buf) {
+  auto store_x = [&](const u32x4_t (&xr)[XPER], int buf, int st) {
 #pragma unroll
     for (int j = 0; j < XPER; ++j) {
       const int p = tid + j * W * 64;
+      const int pc = piece(j);
+      const bool ok = pc / (kStepK / 8) < B && st * kStepK + (pc % (kStepK / 8)) * 8 < K;
       uint16_t* dst = p < XPIECES ? &xs[buf][p / (kStepK / 8)][(p % (kStepK / 8)) * 8]
                                   : &xs_raw[2 * BT * XROW];
-      *reinterpret_cast<u32x4_t*>(dst) = xr[j];
+      *reinterpret_cast<u32x4_t*>(dst) = ok ? xr[j] : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
-  const TileStream<FMT, LAYOUT> ts(codes, scales, min(tile, ntiles - 1), N, K, lane);
+  TileStream<FMT, LAYOUT> ts[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    ts[t] = TileStream<FMT, LAYOUT>(codes, scales, min(tile + t, ntiles - 1), N, K, lane);
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
   const bool xlane = col < BT;
   const int xoff = (xlane ? col : 0) * XROW + grp * 32;
-  f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t acc[TPW][2];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc[t][0] = acc[t][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto load_w = [&](StepFrag<FMT, LAYOUT> (&f)[TPW], int st) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ts[t].load(f[t], st);
+  };
 
   // two buffers; the next step's x loads are issued before its code loads
   // and written to LDS after the current step's math
-  StepFrag<FMT, LAYOUT> fa, fb;
+  StepFrag<FMT, LAYOUT> fa[TPW], fb[TPW];
   u32x4_t xr[XPER];
+  // Issue order is pinned (scheduling barriers): the compiler would
+  // otherwise sink the next step's loads below the current step's math to
+  // save registers -- and then wait for all of them before storing x.
+  auto prefetch = [&](StepFrag<FMT, LAYOUT> (&f)[TPW], int st) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xr, st);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(f, st);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   load_x(xr, 0);
-  ts.load(fa, 0);
-  store_x(xr, 0);
+  load_w(fa, 0);
+  store_x(xr, 0, 0);
   __syncthreads();
   int st = 0;
   for (; st + 2 < nst; st += 2) {
-    load_x(xr, st + 1);
-    ts.load(fb, st + 1);
-    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
-    store_x(xr, (st + 1) & 1);
+    prefetch(fb, st + 1);
+    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
+    store_x(xr, (st + 1) & 1, st + 1);
     __syncthreads();
-    load_x(xr, st + 2);
-    ts.load(fa, st + 2);
-    step_math<FMT, LAYOUT>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc0, acc1);
-    store_x(xr, st & 1);
+    prefetch(fa, st + 2);
+    step_math<FMT, LAYOUT, TPW>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc);
+    store_x(xr, st & 1, st + 2);
     __syncthreads();
   }
   if (st + 1 < nst) {  // two steps left
-    load_x(xr, st + 1);
-    ts.load(fb, st + 1);
-    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
-    store_x(xr, (st + 1) & 1);
+    prefetch(fb, st + 1);
+    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
+    store_x(xr, (st + 1) & 1, st + 1);
     __syncthreads();
-    step_math<FMT, LAYOUT>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+    step_math<FMT, LAYOUT, TPW>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc);
   } else {             // one step left
-    step_math<FMT, LAYOUT>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc0, acc1);
+    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
   }
 
-  store_y(acc0 + acc1, tile, ntiles, N, B, lane, y, ldy);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) store_y(acc[t][0] + acc[t][1], tile + t, ntiles, N, B, lane, y, ldy);
 }
 
-template <int FMT, int LAYOUT, int BT>
+template <int FMT, int LAYOUT, int BT, int TPW = (BT >= 16 ? 2 : 1)>
 hipError_t run(const uint8_t* codes, const void* scales, const float* gs, int64_t N, int64_t K,
                const uint16_t* x, int64_t ldx, int64_t B, uint16_t* y, int64_t ldy,
                hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
-  const unsigned grid = (unsigned)((ntiles + kWaves - 1) / kWaves);
+  const int64_t nwaves = (ntiles + TPW - 1) / TPW;
+  const unsigned grid = (unsigned)((nwaves + kWaves - 1) / kWaves);
   const size_t lds = (2ull * BT * (kStepK + 8) + 8) * sizeof(uint16_t);  // + spare slot
-  gemv_kernel<FMT, LAYOUT, BT><<<grid, kWaves * 64, lds, stream>>>(
+  gemv_kernel<FMT, LAYOUT, BT, TPW><<<grid, kWaves * 64, lds, stream>>>(
       codes, scales, gs, (int)N, (int)K, x, ldx, (int)B, y, ldy);
   return hipGetLastError();
 }
