@@ -281,6 +281,8 @@ hipError_t launch_gemm_w4a16(int fmt, int layout, const uint8_t* codes, const vo
                              const float* gs, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                              int64_t M, uint16_t* C, int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (layout == kLayoutTiled)
+    return launch_gemm_w4a16_tiled(fmt, codes, scales, gs, N, K, A, lda, M, C, ldc, stream);
   const int64_t gy = (M + 16 * MT - 1) / (16 * MT);
   return dispatch_w4a16(fmt, layout, A, lda, M, nullptr, nullptr, gy, M, codes, scales, gs, N, K,
                         C, ldc, stream);

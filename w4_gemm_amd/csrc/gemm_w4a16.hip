@@ -1,0 +1,283 @@
+// gemm_w4a16.hip -- W4A16 GEMM (prefill) for weights in the tiled layout:
+// C[m][n] = sum_k a[m][k] w'[n][k], A bf16 row-major, W' the dequantized
+// INT4 g128 / MXFP4 / NVFP4 weight, fp32 accumulation, bf16 output.
+//
+// W4A16 keeps activations in bf16 and dequantizes the 4-bit weights in
+// registers before a bf16 matrix multiply ("Low-bit inference for very
+// large MoE", table "Kernels on different hardware", row W4A16).  On gfx950
+// the multiply is v_mfma_f32_16x16x32_bf16.
+//
+// The k order inside a super-chunk (128 k) is free, since a dot product
+// does not depend on it: lane l = 16g + n of a 1 KB weight tile holds the
+// 32 codes of row n at k in [32g, 32g+32), and matrix step i (0..3) of the
+// super-chunk takes the codes 8i..8i+8 of every lane -- k = 32g + 8i +
+// [0, 8).  The activation fragment of lane l for step i is then the 16 bytes
+// a[m][32g + 8i + (0..8)] with m = l%16.
+//
+// Work decomposition:
+//   * a workgroup of 8 waves computes a 128 x 512 block of C.  All waves
+//     share the 128 activation rows; wave w owns the 64 columns of weight
+//     tiles 4w..4w+3: 8 x 4 matrix-core tiles, 128 fp32 accumulators per
+//     lane (two waves per SIMD).  Each dequantized weight fragment feeds 8
+//     matrix instructions, which keeps the dequantization (a multiply per
+//     value for NVFP4) off the critical path.
+//   * K advances in stages of 64 (half a super-chunk: steps 2h, 2h+1).  The
+//     activations of a stage (128 rows x 64 k, 16 KB) are gathered into LDS
+//     by direct global->LDS loads in matrix-fragment order -- each load
+//     instruction fills one fragment, lane l fetching exactly the 16 bytes
+//     it will later read -- so every fragment read is one contiguous,
+//     conflict-free kilobyte.  Three buffers, two stages ahead.
+//   * the weight tiles of a super-chunk (the wave's own four, 1 KB each) are
+//     copied verbatim into LDS one super-chunk ahead (two buffers); the
+//     scale words of a group of four super-chunks go straight into registers
+//     (two sets).
+//   * one barrier per stage: each wave waits (explicit vmcnt) for its own
+//     loads of the stage, the barrier makes all activation fragments
+//     visible and frees the buffer the next copies overwrite.  The loop is
+//     unrolled by 8 (one scale group) so every wait count is a constant.
+//   * weights are the matrix instruction's row operand, so a lane ends with
+//     4 consecutive columns of one row of C: 8-byte stores.
+#include "q4_launch.h"
+#include "q4_layout.h"
+#include "q4_mma.h"
+
+#include <type_traits>
+
+namespace q4 {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kRowTiles = 8;                    // 16-row activation tiles per block (128 rows)
+constexpr int kColTiles = 4 * kWaves;           // 16-column weight tiles per block (512 cols)
+constexpr int kAFrags = 2 * kRowTiles;          // activation fragments per stage
+constexpr int kABufs = 3;
+constexpr size_t kSmemBytes = kABufs * kAFrags * 1024 + 2 * kColTiles * 1024;  // 112 KB
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint8_t* lds_base) {
+  // each lane copies 16 bytes from src to lds_base + 16 * lane
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+// Barrier that does not wait for outstanding copies (each wave has waited
+// for its own by count before it); nothing may be moved across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Loads issued for running stage v (group v): the stage's activation
+// fragments (2 per wave), the weight tiles of super-chunk v/2 when v is
+// even (4 per wave), the scale words of scale group v/8 when v % 8 == 0
+// (4 per wave).
+constexpr int group_loads(int v) { return 2 + (v % 2 == 0 ? 4 : 0) + (v % 8 == 0 ? 4 : 0); }
+
+template <int FMT>
+__global__ void __launch_bounds__(kWaves * 64)
+w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
+                   const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                   const float* __restrict__ gs_ptr, int N, int K, uint16_t* __restrict__ C,
+                   int64_t ldc) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t (*abuf)[kAFrags][1024] = reinterpret_cast<uint8_t (*)[kAFrags][1024]>(smem);
+  uint8_t (*wbuf)[kColTiles][1024] =
+      reinterpret_cast<uint8_t (*)[kColTiles][1024]>(smem + kABufs * kAFrags * 1024);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = K >> 7, Q = K >> 9, S2 = 2 * S;   // super-chunks, scale groups, stages
+  const int RTW = (N + 15) >> 4;
+
+  // workgroup -> 128 x 512 block of C: XCD-major, then groups of 4 block rows
+  const int TM = (M + 127) >> 7, TN = (N + 511) >> 9, T = TM * TN;
+  const int b = blockIdx.x;
+  const int lin = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int gsz = 4 * TN, first_m = (lin / gsz) * 4, gm = min(TM - first_m, 4);
+  const int bm = first_m + (lin % gsz) % gm, bn = (lin % gsz) / gm;
+
+  // activation copies: this wave fills the fragments of row tile `wave`
+  // (steps 2h and 2h+1 of each stage); lane l reads row 16*wave + l%16
+  // (clamped) at k = 32(l/16) + 8i within the super-chunk
+  const int arow = min(bm * 128 + 16 * wave + (lane & 15), M - 1);
+  const uint16_t* asrc = A + (int64_t)arow * lda + 32 * (lane >> 4);
+  // this wave's weight tiles (copied and multiplied by it alone)
+  const int wt0 = bn * kColTiles + 4 * wave;
+  // (wave-uniform bases; the lane offsets are added at each load)
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) wsrc[jj] = codes + (int64_t)min(wt0 + jj, RTW - 1) * S * 1024;
+  const int wlane = lane * 16;
+  // this lane's scale bytes of a scale group for weight tile jj: MXFP4 4
+  // bytes (one per super-chunk), NVFP4 8 (two per super-chunk), INT4 4 fp16
+  // of row n = lane%16 (one per super-chunk)
+  constexpr int SW = FMT == 1 ? 1 : 2;  // 32-bit words per tile and group
+  const uint8_t* ssrc[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int64_t t = min(wt0 + jj, RTW - 1);
+    ssrc[jj] = scales + t * Q * (FMT == 0 ? 128 : FMT == 1 ? 256 : 512);
+  }
+  const int slane = FMT == 0 ? (lane & 15) * 8 : FMT == 1 ? lane * 4 : lane * 8;
+  const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
+
+  // scale words of the current scale group and of the next one (loaded
+  // with group 8q, moved into place when the group's first stage starts)
+  uint32_t scur[4][SW], snext[4][SW];
+  auto issue = [&](int v, auto jc) {  // group v; jc = v % 8
+    constexpr int J = decltype(jc)::value;
+    const int vs = min(v, S2 - 1);
+    const int s = vs >> 1, h = vs & 1;
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip)
+      copy16_to_lds(asrc + 128 * s + 8 * (2 * h + ip), abuf[v % kABufs][2 * wave + ip]);
+    if constexpr (J % 2 == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        copy16_to_lds(wsrc[jj] + (int64_t)s * 1024 + wlane, wbuf[(v >> 1) & 1][4 * wave + jj]);
+    }
+    if constexpr (J == 0) {
+      const int q = min(v >> 3, Q - 1);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (SW == 1) {
+          snext[jj][0] = *reinterpret_cast<const uint32_t*>(ssrc[jj] + (int64_t)q * 256 + slane);
+        } else {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(ssrc[jj] + (int64_t)q * (FMT == 0 ? 128 : 512) + slane);
+          snext[jj][0] = w2.x;
+          snext[jj][1] = w2.y;
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[kRowTiles][4];
+#pragma unroll
+  for (int i = 0; i < kRowTiles; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4_t wq[4];  // the wave's weight fragments of the current super-chunk
+
+  // stage u, J = u % 8: wait until only group u+1 may be outstanding,
+  // barrier, issue group u+2 (into the buffers stage u-1 used), multiply.
+  auto iteration = [&](int u, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int H = J & 1;          // half of the super-chunk
+    constexpr int SI = J >> 1;        // super-chunk within the scale group
+    wait_vmcnt_lgkm0<group_loads(J + 1)>();
+    stage_barrier();
+    if constexpr (J == 0) {  // group u/8's scale words have landed (group u is done)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) scur[jj][w] = snext[jj][w];
+    }
+    issue(u + 2, std::integral_constant<int, (J + 2) % 8>());
+    if constexpr (H == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        wq[jj] = *reinterpret_cast<const u32x4_t*>(&wbuf[(u >> 1) & 1][4 * wave + jj][lane * 16]);
+    }
+#pragma unroll
+    for (int ip = 0; ip < 2; ++ip) {
+      const int i = 2 * H + ip;      // matrix step within the super-chunk
+      bf16x8_t wb[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        if constexpr (FMT == 0) {
+          const uint32_t hw = (scur[jj][SI >> 1] >> (16 * (SI & 1))) & 0xFFFFu;
+          wb[jj] = dq8_int4(wq[jj][i], fp16_value(hw));
+        } else if constexpr (FMT == 1) {
+          wb[jj] = dq8_e2m1(wq[jj][i], e8m0_value((scur[jj][0] >> (8 * SI)) & 0xFFu));
+        } else {
+          // the lane's 32 k hold two 16-blocks: steps 0,1 the first, 2,3 the second
+          const uint32_t sb = (scur[jj][SI >> 1] >> (16 * (SI & 1) + 8 * H)) & 0xFFu;
+          wb[jj] = dq8_e2m1_mul(wq[jj][i], e4m3_value(sb) * gs);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRowTiles; ++r) {
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&abuf[u % kABufs][2 * r + ip][lane * 16]));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[r][jj] = mma16x16x32(wb[jj], a, acc[r][jj]);
+      }
+    }
+  };
+
+  issue(0, std::integral_constant<int, 0>());
+  issue(1, std::integral_constant<int, 1>());
+  // K % 512 == 0 in the tiled layout: the stage count is a multiple of 8
+  for (int u0 = 0; u0 < S2; u0 += 8) {
+    iteration(u0, std::integral_constant<int, 0>());
+    iteration(u0 + 1, std::integral_constant<int, 1>());
+    iteration(u0 + 2, std::integral_constant<int, 2>());
+    iteration(u0 + 3, std::integral_constant<int, 3>());
+    iteration(u0 + 4, std::integral_constant<int, 4>());
+    iteration(u0 + 5, std::integral_constant<int, 5>());
+    iteration(u0 + 6, std::integral_constant<int, 6>());
+    iteration(u0 + 7, std::integral_constant<int, 7>());
+  }
+  wait_vmcnt_lgkm0<0>();  // no copy into LDS may still be running at exit
+
+  // tile (r, jj): lane l, register q holds C[m][n] with m = 16r + l%16 and
+  // n = 16jj + 4(l/16) + q -- four consecutive columns of one row
+  const int m0 = bm * 128 + (lane & 15);
+  const int n0 = bn * 512 + 64 * wave + 4 * (lane >> 4);
+#pragma unroll
+  for (int r = 0; r < kRowTiles; ++r) {
+    const int m = m0 + 16 * r;
+    if (m < M) {
+      uint16_t* crow = C + (int64_t)m * ldc;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = n0 + 16 * jj;
+        const f32x4_t v = acc[r][jj];
+        if (n + 3 < N) {
+          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) crow[n + q] = (uint16_t)f32_to_bf16_rne(v[q]);
+        }
+      }
+    }
+  }
+}
+
+template <int FMT>
+hipError_t run(const uint16_t* A, int64_t lda, int64_t M, const uint8_t* codes, const void* scales,
+               const float* gs, int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&w4a16_tiled_kernel<FMT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)kSmemBytes);
+  if (attr != hipSuccess) return attr;
+  const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
+  w4a16_tiled_kernel<FMT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(
+      A, lda, (int)M, codes, static_cast<const uint8_t*>(scales), gs, (int)N, (int)K, C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a16_tiled(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+                                   int64_t N, int64_t K, const uint16_t* A, int64_t lda, int64_t M,
+                                   uint16_t* C, int64_t ldc, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (fmt == 0) return run<0>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 1) return run<1>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
+  return run<2>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
+}
+
+}  // namespace q4

@@ -31,6 +31,12 @@ hipError_t launch_gemm_w4a16(int fmt, int layout, const uint8_t* codes, const vo
                              int64_t N, int64_t K, const uint16_t* A, int64_t lda, int64_t M,
                              uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// W4A16 GEMM with the weight in the tiled layout (K % 512 == 0): the
+// LDS-staged kernel of gemm_w4a16.hip.
+hipError_t launch_gemm_w4a16_tiled(int fmt, const uint8_t* codes, const void* scales, const float* gs,
+                                   int64_t N, int64_t K, const uint16_t* A, int64_t lda, int64_t M,
+                                   uint16_t* C, int64_t ldc, hipStream_t stream);
+
 // W4A4 MXFP4 GEMM C [M][ldc] = A' . W'^T, both MXFP4, K % 128 == 0.
 hipError_t launch_gemm_w4a4(int a_layout, int w_layout, const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
                             const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
