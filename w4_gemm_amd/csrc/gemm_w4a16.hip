@@ -243,9 +243,7 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
         const int n = n0 + 16 * jj;
         const f32x4_t v = acc[r][jj];
         if (n + 3 < N) {
-          const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)

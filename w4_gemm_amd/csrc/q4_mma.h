@@ -34,6 +34,12 @@ __device__ __forceinline__ bf16x8_t dq8_e2m1(uint32_t w, float scale) {
   return as_bf16x8(r);
 }
 
+// Two fp32 values -> packed bf16 pair (low = a), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return as_u32(__builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // 8 E2M1 codes times an arbitrary fp32 scale (NVFP4: E4M3 * gs) -> 8 bf16:
 // exact fp32 code values, one fp32 multiply, one rounding to bf16.
 __device__ __forceinline__ bf16x8_t dq8_e2m1_mul(uint32_t w, float scale) {
@@ -45,7 +51,7 @@ __device__ __forceinline__ bf16x8_t dq8_e2m1_mul(uint32_t w, float scale) {
     else if (j == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
     else if (j == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
     else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    r[j] = f32_to_bf16_rne(v[0] * scale) | (f32_to_bf16_rne(v[1] * scale) << 16);
+    r[j] = pk_bf16(v[0] * scale, v[1] * scale);
   }
   return as_bf16x8(r);
 }
@@ -63,7 +69,7 @@ __device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) {
   for (int j = 0; j < 4; ++j) {
     const float e0 = __builtin_fmaf((float)((lo >> (8 * j)) & 0xFFu), s, m8);
     const float e1 = __builtin_fmaf((float)((hi >> (8 * j)) & 0xFFu), s, m8);
-    r[j] = f32_to_bf16_rne(e0) | (f32_to_bf16_rne(e1) << 16);
+    r[j] = pk_bf16(e0, e1);
   }
   return as_bf16x8(r);
 }
