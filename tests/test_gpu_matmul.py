@@ -268,7 +268,8 @@ def _grouped_case(E, N, K, T, topk, seed, fmt="mxfp4"):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("E,N,K,T,topk", [(8, 200, 512, 50, 2), (16, 128, 256, 300, 4),
-                                          (4, 72, 128, 3, 1), (8, 144, 1024, 70, 3)])
+                                          (4, 72, 128, 3, 1), (8, 144, 1024, 70, 3),
+                                          (4, 272, 512, 300, 2)])   # ~150 rows per expert
 def test_grouped_small(fmt, E, N, K, T, topk, layout):
     if layout == "tiled" and not tiled_ok(K, N):
         pytest.skip("the tiled layout needs K % 512 == 0 and N % 16 == 0")
@@ -292,12 +293,13 @@ def test_grouped_small(fmt, E, N, K, T, topk, layout):
                          EXACT[fmt], f"grouped {fmt} expert {e}")
 
 
-def test_grouped_empty_experts_and_bad_gather():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_grouped_empty_experts_and_bad_gather(layout):
     """Experts with no rows are skipped; a gather index outside [0, T)
     produces a zero row; offsets beyond P are clamped."""
-    E, N, K, T = 4, 64, 256, 10
+    E, N, K, T = 4, 64, 512, 10
     w, a, _ = _grouped_case(E, N, K, T, 1, 61)
-    qg, qr = quantized(w, "mxfp4")
+    qg, qr = quantized(w, "mxfp4", layout)
     gather = np.array([0, 1, 2, 99, 3, -5, 4], np.int32)     # rows 3 and 5 invalid
     offsets = np.array([0, 3, 3, 7, 7], np.int32)            # experts 1 and 3 empty
     C = torch.full((7, N), float("nan"), dtype=torch.bfloat16, device=DEV)

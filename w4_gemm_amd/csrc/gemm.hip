@@ -293,6 +293,9 @@ hipError_t launch_grouped(int fmt, int layout, const uint16_t* A, int64_t lda, i
                           const uint8_t* codes, const void* scales, const float* gs, int64_t N,
                           int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
   if (E == 0 || N == 0 || P == 0) return hipSuccess;
+  if (layout == kLayoutTiled && T > 0)
+    return launch_grouped_tiled(fmt, A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc,
+                                stream);
   return dispatch_w4a16(fmt, layout, A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C,
                         ldc, stream);
 }

@@ -48,6 +48,13 @@ hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scale
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// Grouped expert GEMM with the expert weights in the tiled layout (K % 512
+// == 0, N % 16 == 0, T > 0): the weight-streaming kernel of grouped.hip.
+hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather,
+                                const int32_t* offsets, int32_t E, int64_t P, const uint8_t* codes,
+                                const void* scales, const float* gs, int64_t N, int64_t K, uint16_t* C,
+                                int64_t ldc, hipStream_t stream);
+
 // Grouped expert GEMM (W4A16), see q4_grouped_gemm.
 hipError_t launch_grouped(int fmt, int layout, const uint16_t* A, int64_t lda, int64_t T,
                           const int32_t* gather, const int32_t* offsets, int32_t E, int64_t P,
