@@ -150,6 +150,138 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
   }
 }
 
+// Block-mapped quantizer for cols % 128 == 0 (every tiled tensor): a
+// workgroup of 4 waves takes 16 rows x 512 k.  The rows are first staged in
+// LDS with fully coalesced loads (each wave instruction reads 1 KB of one
+// row); then lane l = 16g + n of wave s takes row n, k = 128s + 32g .. +32 --
+// one MXFP4 block, two NVFP4 blocks, a quarter INT4 group (completed by a
+// max over the 4 lanes of the row) -- and writes its 16 code bytes with one
+// store.  In the tiled layout those 64 stores are exactly tile s: one
+// contiguous kilobyte per wave.  Rows past the end are staged as zeros (the
+// tiled padding rows) and not stored in the row-major layout.
+template <int FMT, int LAYOUT>
+__global__ void __launch_bounds__(kThreads)
+quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+                      uint8_t* __restrict__ codes, void* __restrict__ scales,
+                      const float* gs_src, int gs_is_amax, float* gs_out) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[16][512 + 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t KB = (cols + 511) >> 9;
+  const int64_t band = blockIdx.x / KB, kb = blockIdx.x - band * KB;
+  const int64_t r0 = band * 16, k0 = kb * 512;
+
+  float gs = 0.0f;
+  if constexpr (FMT == 2) {
+    if (gs_is_amax) {
+      gs = fmaxf(u2f(*reinterpret_cast<const uint32_t*>(gs_src)), 1e-12f) / 2688.0f;
+    } else {
+      gs = *gs_src;
+      if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 4 * j + wave;
+    const int64_t k = k0 + 8 * lane;
+    const bool ok = r0 + row < rows && k < cols;
+    const uint4 v = ok ? *reinterpret_cast<const uint4*>(src + (r0 + row) * ld + k) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(&xs[row][8 * lane]) = v;
+  }
+  __syncthreads();
+  const int64_t S = cols >> 7;
+  const int64_t s = kb * 4 + wave;  // super-chunk of this wave
+  if (s >= S) return;               // (row-major, cols % 512 != 0); no barrier follows
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t r = r0 + n;
+  Chunk8 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(&xs[n][128 * wave + 32 * g + 8 * i]);
+    x[i].v[0] = bf16_lo(raw.x); x[i].v[1] = bf16_hi(raw.x);
+    x[i].v[2] = bf16_lo(raw.y); x[i].v[3] = bf16_hi(raw.y);
+    x[i].v[4] = bf16_lo(raw.z); x[i].v[5] = bf16_hi(raw.z);
+    x[i].v[6] = bf16_lo(raw.w); x[i].v[7] = bf16_hi(raw.w);
+  }
+  const bool store = LAYOUT == kLayoutTiled || r < rows;
+  const int64_t Q = cols >> 9;
+  const int64_t q = s >> 2, si = s & 3;
+  uint32_t packed[4];
+  if constexpr (FMT == 0) {
+    float amax = fmaxf(fmaxf(absmax8(x[0]), absmax8(x[1])), fmaxf(absmax8(x[2]), absmax8(x[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const uint32_t sbits = fp16_encode(amax / 7.0f);
+    const float sc = fp16_value(sbits);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t p = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int qv = 0;
+        if (sc != 0.0f) {
+          float qr = __builtin_rintf(x[i].v[j] / sc);
+          qr = fminf(fmaxf(qr, -8.0f), 7.0f);
+          qv = (int)qr;
+        }
+        p |= ((uint32_t)qv & 0xFu) << (4 * j);
+      }
+      packed[i] = p;
+    }
+    if (store && g == 0) {
+      uint16_t* sp = reinterpret_cast<uint16_t*>(scales);
+      if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 16 + n) * 4 + si] = (uint16_t)sbits;
+      else sp[r * S + s] = (uint16_t)sbits;
+    }
+  } else if constexpr (FMT == 1) {
+    const float amax = fmaxf(fmaxf(absmax8(x[0]), absmax8(x[1])), fmaxf(absmax8(x[2]), absmax8(x[3])));
+    const uint32_t e = mx_e8m0(amax);
+    const float sc = e8m0_value(e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[i] = e2m1_pack8(x[i], sc);
+    if (store) {
+      uint8_t* sp = reinterpret_cast<uint8_t*>(scales);
+      if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 64 + lane) * 4 + si] = (uint8_t)e;
+      else sp[r * (cols >> 5) + 4 * s + g] = (uint8_t)e;
+    }
+  } else {
+    uint32_t sc2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float amax = fmaxf(absmax8(x[2 * h]), absmax8(x[2 * h + 1]));
+      const float t = fminf((amax / 6.0f) / gs, 448.0f);
+      const uint32_t sc = e4m3_encode(t);
+      const float eff = e4m3_value(sc) * gs;
+      sc2[h] = sc;
+#pragma unroll
+      for (int i = 2 * h; i < 2 * h + 2; ++i) {
+        if (eff == 0.0f) {  // E4M3 scale underflowed to 0: magnitude codes 0, signs kept
+          uint32_t p = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) p |= ((f2u(x[i].v[j]) >> 31) << 3) << (4 * j);
+          packed[i] = p;
+        } else {
+          Chunk8 y;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y.v[j] = x[i].v[j] / eff;  // fp32 division by the scale as used
+          packed[i] = e2m1_pack8(y, 1.0f);
+        }
+      }
+    }
+    if (store) {
+      uint16_t* sp = reinterpret_cast<uint16_t*>(scales);  // the lane's two E4M3 bytes, first block low
+      const uint16_t pair = (uint16_t)(sc2[0] | (sc2[1] << 8));
+      if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 64 + lane) * 4 + si] = pair;
+      else sp[(r * (cols >> 4) + 8 * s + 2 * g) >> 1] = pair;
+    }
+  }
+  if (store) {
+    uint8_t* dst = LAYOUT == kLayoutTiled ? codes + ((band * S + s) << 10) + lane * 16
+                                          : codes + r * (cols >> 1) + 64 * s + 16 * g;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
 // Tensor absmax for NVFP4: max |w| over rows x cols, folded into *amax_bits
 // with an atomic max on the fp32 bits (non-negative floats order like their
 // bit patterns, and max is exact, so the result does not depend on order).
@@ -238,20 +370,35 @@ unsigned grid_for(int64_t chunks) {
   return (unsigned)b;
 }
 
+// Quantize kernel launch: the block-mapped kernel when cols % 128 == 0,
+// else the lane-per-8-values kernel.
+template <int FMT, int LAYOUT>
+void launch_q(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols, uint8_t* codes,
+              void* scales, const float* gs_src, int gs_is_amax, float* gs_out, hipStream_t stream) {
+  if (cols % 128 == 0) {
+    const int64_t blocks = ((stored_rows<LAYOUT>(rows) + 15) / 16) * ((cols + 511) / 512);
+    quantize_block_kernel<FMT, LAYOUT><<<(unsigned)blocks, kThreads, 0, stream>>>(
+        src, ld, rows, cols, codes, scales, gs_src, gs_is_amax, gs_out);
+  } else {
+    const unsigned grid = grid_for(stored_rows<LAYOUT>(rows) * (cols >> 3));
+    quantize_kernel<FMT, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales,
+                                                               gs_src, gs_is_amax, gs_out);
+  }
+}
+
 template <int LAYOUT>
 hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t rows, int64_t cols,
                            uint8_t* codes, void* scales, float* gs, const float* gs_in,
                            hipStream_t stream) {
   const int64_t chunks = stored_rows<LAYOUT>(rows) * (cols >> 3);
-  const unsigned grid = grid_for(chunks);
   if (fmt == 0) {
-    if (chunks) quantize_kernel<0, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+    if (chunks) launch_q<0, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
   } else if (fmt == 1) {
-    if (chunks) quantize_kernel<1, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr);
+    if (chunks) launch_q<1, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
   } else {
     if (gs_in) {
       if (chunks) {
-        quantize_kernel<2, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs_in, 0, gs);
+        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs_in, 0, gs, stream);
       } else {
         // nothing to quantize: still record the caller's gs
         hipError_t e = hipMemcpyAsync(gs, gs_in, sizeof(float), hipMemcpyDeviceToDevice, stream);
@@ -267,7 +414,7 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
           const unsigned agrid = sgrid < 2048 ? sgrid : 2048;
           absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
         }
-        quantize_kernel<2, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales, gs, 1, nullptr);
+        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, 1, nullptr, stream);
       }
       finalize_gs_kernel<<<1, 1, 0, stream>>>(gs);
     }
