@@ -288,14 +288,21 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
 __global__ void __launch_bounds__(kThreads)
 absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
               uint32_t* amax_bits) {
-  const int64_t cpr = cols >> 3;
-  const int64_t total = rows * cpr;
+  // rows over workgroups, a row's 16-byte chunks over the threads (no
+  // division per element); four independent loads in flight per thread
+  const int cpr = (int)(cols >> 3);
   float a = 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
-       c += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = c / cpr;
-    const int64_t k0 = (c - r * cpr) * 8;
-    a = fmaxf(a, absmax8(load8(src + r * ld + k0, true)));
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* row = src + r * ld;
+    int c = threadIdx.x;
+    for (; c + 3 * kThreads < cpr; c += 4 * kThreads) {
+      Chunk8 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = load8(row + (int64_t)(c + u * kThreads) * 8, true);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a = fmaxf(a, absmax8(x[u]));
+    }
+    for (; c < cpr; c += kThreads) a = fmaxf(a, absmax8(load8(row + (int64_t)c * 8, true)));
   }
   a = group_max<64>(a);
   __shared__ float part[kThreads / 64];
@@ -408,10 +415,8 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
       uint32_t* amax = reinterpret_cast<uint32_t*>(gs);
       set_word_kernel<<<1, 1, 0, stream>>>(amax, 0u);
       if (chunks) {
-        const int64_t src_chunks = rows * (cols >> 3);
-        if (src_chunks) {
-          const unsigned sgrid = grid_for(src_chunks);
-          const unsigned agrid = sgrid < 2048 ? sgrid : 2048;
+        if (rows > 0 && cols > 0) {
+          const unsigned agrid = (unsigned)(rows < 2048 ? rows : 2048);
           absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
         }
         launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, 1, nullptr, stream);
