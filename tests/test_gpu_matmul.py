@@ -44,7 +44,7 @@ def test_gemv_small(fmt, N, K, layout):
     w = workloads.matrix(f"tg/w{N}x{K}", N, K, 0.02, seed=21, outlier_frac=0.001, outlier_mult=20.0)
     qg, qr = quantized(w, fmt, layout)
     wd = oracle.dequant(qr)
-    for B in (1, 3, 16):
+    for B in (1, 3, 9, 16):
         x = workloads.matrix(f"tg/x{B}x{K}", B, K, 1.0, seed=22)
         y = torch.full((B, N + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
         q4.q4_gemv(qg, x.to(DEV), y[:, :N])
@@ -161,7 +161,8 @@ def test_full_mxfp4_decode_gemv(layout):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (1, 1000, 1024), (333, 520, 1152)])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (1, 1000, 1024), (333, 520, 1152),
+                                   (130, 1030, 2048), (256, 512, 4096)])
 def test_gemm_w4a16_small(fmt, M, N, K, layout):
     if layout == "tiled" and not tiled_ok(K):
         pytest.skip("the tiled layout needs K % 512 == 0")
@@ -204,7 +205,7 @@ def test_full_nvfp4_prefill_gemm(layout):
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("alayout,wlayout", [("rows", "rows"), ("tiled", "tiled"),
                                              ("rows", "tiled"), ("tiled", "rows")])
-@pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (129, 1000, 1024)])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (129, 1000, 1024), (65, 1030, 2048)])
 def test_gemm_w4a4_small(M, N, K, alayout, wlayout):
     if "tiled" in (alayout, wlayout) and not tiled_ok(K):
         pytest.skip("the tiled layout needs K % 512 == 0")
