@@ -35,6 +35,19 @@ def test_quantize_small_random(fmt, shape):
     assert_quant_equal(qg, qr, fmt)
 
 
+@pytest.mark.parametrize("fmt,shape", [("mxfp4", (5, 96)), ("mxfp4", (33, 224)), ("nvfp4", (3, 48)),
+                                       ("nvfp4", (40, 208))])
+def test_quantize_row_major_short_rows(fmt, shape):
+    """Row lengths that are not a multiple of 128 (MXFP4 % 32, NVFP4 % 16):
+    the lane-per-8-values quantizer."""
+    log("quantize short rows", fmt, shape)
+    rows, cols = shape
+    w = workloads.matrix(f"tq/{rows}x{cols}", rows, cols, 0.02, seed=12,
+                         outlier_frac=0.01, outlier_mult=25.0)
+    qg, qr = quant_both(w, fmt)
+    assert_quant_equal(qg, qr, fmt)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", [(1, 512), (16, 512), (37, 1024), (130, 1536), (257, 512)])
 def test_quantize_small_random_tiled(fmt, shape):
