@@ -91,6 +91,17 @@ class GraphTimer:
     def per_launch_ms(self, replays, warmup=3):
         return self.replay_ms(replays, warmup) / self.per_graph
 
+    def per_launch_ms_each(self, replays):
+        """Per-launch time of each replay separately (for a median)."""
+        t = self.torch
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(replays)]
+        for s, e in ev:
+            s.record()
+            self.graph.replay()
+            e.record()
+        t.cuda.synchronize()
+        return [s.elapsed_time(e) / self.per_graph for s, e in ev]
+
 
 def timed(torch, fn, iters, warmup=1, replays=3):
     """Average per-launch time of fn() from a graph of `iters` launches,
@@ -182,8 +193,10 @@ def main():
         gt = GraphTimer(torch, lambda i, b=b: q4.q4_gemv(copies[i % ncopy], xs[b], ys[b]),
                         per_graph=ncopy * 4)
         ms = gt.per_launch_ms(max(3, args.steps // (ncopy * 4)))
+        each = sorted(gt.per_launch_ms_each(9))
         alg = wbytes + b * K * 2 + b * N * 2
-        per_b[b] = {"us": ms * 1e3, "weight_GBps": wbytes / (ms * 1e-3) / 1e9,
+        per_b[b] = {"us": ms * 1e3, "us_median": each[len(each) // 2] * 1e3,
+                    "weight_GBps": wbytes / (ms * 1e-3) / 1e9,
                     "alg_GBps": alg / (ms * 1e-3) / 1e9, "alg_bytes": alg}
     dom = max(batches, key=lambda b: per_b[b]["us"])
     achieved = per_b[dom]["alg_GBps"]
@@ -197,10 +210,19 @@ def main():
                 traffic = rec["bytes_per_launch"][str(dom)]
         except Exception:
             traffic = None
+    # a measured device-to-device copy of 1 GB (1 GB read + 1 GB written),
+    # reported beside the published peak as context
+    csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    copy_ms = timed(torch, lambda: cdst.copy_(csrc), 4, warmup=1, replays=3)
+    copy_gbs = 2 * csrc.numel() / (copy_ms * 1e-3) / 1e9
+    del csrc, cdst
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"gemv_kernel<MXFP4> B={dom}", "alg_bytes_per_launch": per_b[dom]["alg_bytes"],
-                "avg_launch_us": round(per_b[dom]["us"], 3)}
+                "avg_launch_us": round(per_b[dom]["us"], 3),
+                "device_copy_GBps": round(copy_gbs, 1),
+                "frac_of_device_copy": round(achieved / copy_gbs, 4)}
 
     extra = {"decode_gemv_per_batch": {str(b): {k: round(v, 3) for k, v in per_b[b].items()}
                                        for b in batches},
