@@ -14,6 +14,9 @@ definitions in fp64 on the oracle's own dequantized weights:
     for very large MoE", table "Kernels on different hardware", row W4A16).
   * W4A4 MXFP4: both operands MXFP4-quantized along K, then the same sum on
     the dequantized values (same table, row W4A4).
+  * W4A8: INT4 weights, activations quantized to FP8 E4M3 with one scale
+    per token (formats.py fp8_per_row, "Quantization in deployment"), then
+    the same sum on both dequantized operands (same table, row W4A8).
   * Grouped MoE GEMM: one low-bit weight matrix per expert, each routed row
     multiplied by its expert's matrix (same page, "A few details", MoE
     grouped GEMM bullet).
@@ -77,6 +80,14 @@ def lib():
         L.oracle_quantize_mxfp4.restype = ctypes.c_int
         L.oracle_quantize_nvfp4.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _p]
         L.oracle_quantize_nvfp4.restype = ctypes.c_int
+        L.oracle_fp8_row_scale.argtypes = [ctypes.c_float]
+        L.oracle_fp8_row_scale.restype = ctypes.c_float
+        L.oracle_fp8_code.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.oracle_fp8_code.restype = ctypes.c_int
+        L.oracle_quantize_fp8_rows.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+        L.oracle_quantize_fp8_rows.restype = None
+        L.oracle_dequant_fp8_rows.argtypes = [_p, _p, _i64, _i64, _p]
+        L.oracle_dequant_fp8_rows.restype = None
         L.oracle_dequant_int4.argtypes = [_p, _p, _i64, _i64, _i64, _p]
         L.oracle_dequant_int4.restype = None
         L.oracle_dequant_mxfp4.argtypes = [_p, _p, _i64, _i64, _p]
@@ -267,6 +278,59 @@ def gemm_w4a4(a, q: QTensor, rows=None, aq: QTensor | None = None) -> np.ndarray
         aq = QTensor("mxfp4", len(rows), aq.cols, aq.codes[np.asarray(rows)],
                      aq.scales[np.asarray(rows)])
     return matmul_f64(dequant(aq), dequant(q))
+
+
+class FP8Rows:
+    """Oracle-side FP8 activations: E4M3 codes [rows, cols] (row-major) and
+    one fp32 scale per row."""
+
+    def __init__(self, rows, cols, codes, scales):
+        self.rows, self.cols, self.codes, self.scales = rows, cols, codes, scales
+
+
+def quantize_fp8_rows(a) -> FP8Rows:
+    """Per-token FP8 quantization (formats.py fp8_per_row, "Quantization in
+    deployment"): scale = max(amax_row, 1e-12)/448, E4M3 of clamp(x/scale)."""
+    a = _f32(a)
+    rows, cols = a.shape
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros(rows, dtype=np.float32)
+    lib().oracle_quantize_fp8_rows(_ptr(a), rows, cols, cols, _ptr(codes), _ptr(scales))
+    return FP8Rows(rows, cols, codes, scales)
+
+
+def fp8_row_scale(amax: float) -> float:
+    return float(lib().oracle_fp8_row_scale(float(amax)))
+
+
+def fp8_code(x: float, s: float) -> int:
+    return int(lib().oracle_fp8_code(float(x), float(s)))
+
+
+def dequant_fp8_rows(q: FP8Rows) -> np.ndarray:
+    """fp32(E4M3 value * row scale)."""
+    out = np.empty((q.rows, q.cols), dtype=np.float32)
+    codes = np.ascontiguousarray(q.codes)
+    scales = np.ascontiguousarray(q.scales, dtype=np.float32)
+    lib().oracle_dequant_fp8_rows(_ptr(codes), _ptr(scales), q.rows, q.cols, _ptr(out))
+    return out
+
+
+def gemm_w4a8(a, q: QTensor, rows=None, aq: FP8Rows | None = None) -> np.ndarray:
+    """W4A8 GEMM: C = deq(fp8_per_row(A)) deq(W)^T in fp64, W INT4 g128
+    ("Low-bit inference for very large MoE", table "Kernels on different
+    hardware", row W4A8: INT4 weights, activations quantized to FP8)."""
+    if q.fmt != "int4":
+        raise ValueError("W4A8 is defined for INT4 weights")
+    if aq is None:
+        a = _f32(a)
+        if rows is not None:
+            a = np.ascontiguousarray(a[np.asarray(rows)])
+        aq = quantize_fp8_rows(a)
+    elif rows is not None:
+        r = np.asarray(rows)
+        aq = FP8Rows(len(r), aq.cols, aq.codes[r], aq.scales[r])
+    return matmul_f64(dequant_fp8_rows(aq), dequant(q))
 
 
 def grouped_gemm(a, gather, offsets, q_all: QTensor, n: int, experts=None) -> np.ndarray:

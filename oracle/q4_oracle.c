@@ -21,6 +21,9 @@
  *   - "Quantization chains" (inferenceinterviews.com), sections "Bits per
  *     weight", "E4M3 against E5M2" (max 448, min normal 2^-6, min subnormal
  *     2^-9) and "MXFP4 against NVFP4 scales".
+ *   - for the W4A8 activations: "Quantization in deployment", formats.py
+ *     fp8() / fp8_per_row() (one E4M3 scale per token, amax / 448, clamp to
+ *     +-448), and "Quantization chains", "One outlier sets the scale".
  *
  * Readings where the pages leave a step open (each one is listed with its
  * justification in the design notes of the repository):
@@ -394,6 +397,63 @@ void oracle_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, float gs,
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 with one fp32 scale per row: the activation side of W4A8.        */
+/* "Quantization in deployment", formats.py fp8() and fp8_per_row(): each    */
+/* row (token) gets scale = max(amax_row, 1e-12) / 448; every value is       */
+/* divided by it, clamped to +-448 and rounded to the nearest E4M3 value.    */
+/* Readings: rounding is to nearest, ties to the even code (torch's          */
+/* float8_e4m3fn cast, which fp8() calls); the sign bit of the input is      */
+/* kept, so -0 and negatives that round to 0 give 0x80.                      */
+/* ------------------------------------------------------------------------ */
+
+/* Row scale of a row whose largest magnitude is amax. */
+float oracle_fp8_row_scale(float amax)
+{
+    float a = amax > 1e-12f ? amax : 1e-12f;
+    return a / 448.0f;
+}
+
+/* E4M3 code (with sign) of x for a row scale s. */
+int oracle_fp8_code(float x, float s)
+{
+    float y = x / s;
+    float t = fabsf(y);
+    if (t > 448.0f)
+        t = 448.0f;
+    return (signbit_f(y) << 7) | oracle_e4m3_code(t);
+}
+
+void oracle_quantize_fp8_rows(const float* w, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* codes, float* scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* x = w + r * ld;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < cols; ++k)
+            if (fabsf(x[k]) > amax)
+                amax = fabsf(x[k]);
+        float s = oracle_fp8_row_scale(amax);
+        scales[r] = s;
+        for (int64_t k = 0; k < cols; ++k)
+            codes[r * cols + k] = (uint8_t)oracle_fp8_code(x[k], s);
+    }
+}
+
+/* value = fp32(E4M3 value * row scale), the product fp8() returns. */
+void oracle_dequant_fp8_rows(const uint8_t* codes, const float* scales, int64_t rows,
+                             int64_t cols, float* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k) {
+            int c = codes[r * cols + k];
+            float v = oracle_e4m3_value(c) * scales[r];
+            out[r * cols + k] = (c & 0x80) ? -v : v;
+        }
+}
+
 /* fp32 array -> bf16 array (round to nearest even). */
 void oracle_f32_to_bf16_array(const float* in, int64_t n, uint16_t* out)
 {
@@ -402,4 +462,4 @@ void oracle_f32_to_bf16_array(const float* in, int64_t n, uint16_t* out)
         out[i] = oracle_f32_to_bf16(in[i]);
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }
