@@ -31,6 +31,7 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 matrix cores
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
 METRIC = "W4 GEMV weight GB/s and W4 GEMM TFLOP/s vs MI355X roofline, 1 GPU"
 
 
@@ -259,6 +260,8 @@ def main():
         extra["moe_grouped_mxfp4_64x2048x7168"] = bench_moe(torch, q4, workloads, dev, args.seed)
     if want("w4a4"):
         extra["w4a4_mxfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed)
+    if want("w4a8"):
+        extra["w4a8_int4_fp8_gemm_4096x8192x8192"] = bench_w4a8(torch, q4, workloads, dev, args.seed)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -358,6 +361,25 @@ def bench_w4a4(torch, q4, workloads, dev, seed):
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
             "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+            "act_quantize_us": round(ams * 1e3, 1),
+            "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+
+
+def bench_w4a8(torch, q4, workloads, dev, seed):
+    log("generating the W4A8 workload (4096 x 8192 x 8192)")
+    wl = workloads.w4a8_gemm(seed=seed)
+    A = wl.tensors["A"].to(dev)
+    W = wl.tensors["W"].to(dev)
+    M, K = A.shape
+    N = W.shape[0]
+    qw = q4.quantize(W, "int4", layout="tiled")
+    qa = q4.quantize(A, "fp8_row", layout="tiled")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(torch, lambda: q4.q4_gemm(qa, qw, C), 10, 2)
+    ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+            "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
             "act_quantize_us": round(ams * 1e3, 1),
             "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
 

@@ -18,8 +18,15 @@
  *                 block scale = E4M3(min(amax_b/6/gs, 448)), element
  *                 divided by E4M3(scale)*gs.  ("Quantization in deployment",
  *                 formats.py nvfp4(); "Quantization chains", NVFP4 vs MXFP4.)
- * Every rounding is to nearest, ties to the even code; E2M1 keeps the sign
- * bit of the input; a block whose stored scale is 0 has magnitude codes 0.
+ *   Q4_FP8_ROW    the activation operand of W4A8, not a weight format:
+ *                 one E4M3 byte per value and one fp32 scale per row
+ *                 (token), scale = max(amax_row,1e-12)/448, code =
+ *                 E4M3(clamp(x/scale, +-448)).  ("Quantization in
+ *                 deployment", formats.py fp8() per row; "Quantization
+ *                 chains", "One outlier sets the scale".)
+ * Every rounding is to nearest, ties to the even code; E2M1 and E4M3 keep
+ * the sign bit of the input; a block whose stored scale is 0 has magnitude
+ * codes 0.
  *
  * Layouts of a quantized tensor (q4_tensor); all device memory is owned by
  * the caller.  Within a byte, element k sits in bits 3:0 when k is even and
@@ -47,6 +54,16 @@
  *           INT4:  fp16 element ((t*Q + q)*16 + n)*4 + i is the scale of
  *                  row 16t+n, 128-group 4q + i          (RT*Q*128 bytes).
  *   Padding rows (16t+n >= rows) hold the quantization of zeros.
+ *
+ * Q4_FP8_ROW in the two layouts (cols % 16 == 0 row-major, % 512 tiled):
+ *   row-major  codes uint8 [rows][cols] (E4M3 bytes, sign in bit 7).
+ *   tiled      RT*S tiles of 2048 bytes, tile (t, s) at (t*S + s)*2048.
+ *              Lane l = 16g + n owns 32 operand bytes of row 16t+n:
+ *              operand byte 4d + i (dword d = 2w + h, w = 0..3, h = 0..1,
+ *              i = 0..3) holds k = 128s + 32g + 8w + 2i + h.  Operand
+ *              bytes 0..15 of lane l sit at tile byte 16l, operand bytes
+ *              16..31 at 1024 + 16l.  Padding rows hold code 0.
+ *   scales     fp32 [rows] in both layouts; global_scale is NULL.
  *
  *   global_scale  NVFP4 only: device fp32[1], the multiplier gs; else NULL.
  *
@@ -77,7 +94,8 @@ extern "C" {
 typedef enum q4_format {
     Q4_INT4_G128 = 0,
     Q4_MXFP4 = 1,
-    Q4_NVFP4 = 2
+    Q4_NVFP4 = 2,
+    Q4_FP8_ROW = 3
 } q4_format;
 
 typedef enum q4_layout {
@@ -133,7 +151,8 @@ q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* code
  * gs; otherwise gs is computed from the whole matrix (one extra read pass)
  * and written to dst->global_scale.  nv_global_in must be NULL for the other
  * formats.  rows == 0 or cols == 0 is a no-op (for NVFP4 without
- * nv_global_in, gs is still written: max(0,1e-12)/2688).
+ * nv_global_in, gs is still written: max(0,1e-12)/2688).  Q4_FP8_ROW
+ * quantizes each row with its own scale (the W4A8 activations).
  */
 q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
                       const float* nv_global_in, void* stream);
@@ -166,7 +185,15 @@ q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx
  *                       bf16 matrix cores (same table, row W4A16);
  *   A_q (MXFP4, rows M, cols K) with W MXFP4 -> W4A4: both operands enter
  *                       the block-scaled FP4 matrix cores directly (same
- *                       table, row W4A4).  Other formats: Q4_ERR_FORMAT.
+ *                       table, row W4A4);
+ *   A_q (Q4_FP8_ROW, rows M, cols K) with W INT4 -> W4A8: the INT4 codes
+ *                       become exact E4M3 values, the products run on FP8
+ *                       matrix cores, and each 128-wide group's partial sum
+ *                       is multiplied by its fp16 weight scale in fp32 (same
+ *                       table, row W4A8; "Quantization in deployment", the
+ *                       per-block promotion of block-scaled FP8 GEMMs);
+ *                       C = s_a[m] * sum_g s_w[n][g] * sum_(k in g) a8*q.
+ * Other format pairs, and a Q4_FP8_ROW W: Q4_ERR_FORMAT.
  * K = W->cols must be a multiple of 128.  M == 0 or N == 0 is a no-op.
  */
 q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A_q,

@@ -138,6 +138,26 @@ def test_gemm_validation():
     assert L.q4_gemm(0, A16, 512, None, ctypes.byref(w), A16, 512, None) == OK
 
 
+def test_fp8_rows_sizes_and_formats():
+    assert q4.q4_sizes(q4.FP8_ROW, 3, 1024) == (3 * 1024, 3 * 4)
+    assert q4.q4_sizes(q4.FP8_ROW, 3, 1024, "tiled") == (16 * 1024, 3 * 4)
+    with pytest.raises(q4.Q4Error):
+        q4.q4_sizes(q4.FP8_ROW, 3, 1000)
+    L = q4.lib()
+    w4 = desc(fmt=q4.INT4_G128, rows=512, cols=512)
+    mx = desc(fmt=q4.MXFP4, rows=512, cols=512)
+    a8 = desc(fmt=q4.FP8_ROW, rows=64, cols=512)
+    # W4A8 needs an INT4 weight; an FP8 tensor is never a weight
+    assert L.q4_gemm(64, None, 0, ctypes.byref(a8), ctypes.byref(mx), A16, 512, None) == FMT
+    assert L.q4_gemm(64, None, 0, ctypes.byref(a8), ctypes.byref(a8), A16, 512, None) == FMT
+    assert L.q4_gemm(64, A16, 512, None, ctypes.byref(a8), A16, 512, None) == FMT
+    assert L.q4_gemm(32, None, 0, ctypes.byref(a8), ctypes.byref(w4), A16, 512, None) == SHAPE
+    assert L.q4_gemm(0, None, 0, ctypes.byref(desc(fmt=q4.FP8_ROW, rows=0, cols=512)),
+                     ctypes.byref(w4), A16, 512, None) == OK
+    assert L.q4_gemv(ctypes.byref(a8), A16, 1, 512, A16, 512, None) == FMT
+    assert L.q4_quantize(A16, 512, ctypes.byref(a8), A16, None) == FMT   # no global scale input
+
+
 def test_grouped_validation():
     L = q4.lib()
     w = desc(rows=8 * 128, cols=512)

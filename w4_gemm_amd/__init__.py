@@ -1,5 +1,6 @@
 """w4_gemm_amd -- 4-bit absmax block quantization (INT4 g128, MXFP4, NVFP4)
-and the W4 matmuls that consume it, as hand-written HIP kernels for gfx950.
+and the W4 matmuls that consume it (W4A16, W4A4, W4A8 with per-token FP8
+activations), as hand-written HIP kernels for gfx950.
 
 This module is the thin Python binding of libq4.so's C ABI (include/q4.h):
 the functions have the same names and only marshal arguments -- torch
@@ -17,17 +18,17 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "INT4_G128", "MXFP4", "NVFP4", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
+    "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
     "q4_grouped_gemm", "empty_q4", "quantize", "LIB_PATH",
 ]
 
-INT4_G128, MXFP4, NVFP4 = 0, 1, 2
-FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4}
+INT4_G128, MXFP4, NVFP4, FP8_ROW = 0, 1, 2, 3
+FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4, "fp8_row": FP8_ROW}
 LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 LAYOUT_NAMES = {"rows": LAYOUT_ROWS, "tiled": LAYOUT_TILED}
-GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16}
+GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16, FP8_ROW: 16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
@@ -129,6 +130,8 @@ class Q4Tensor:
     Tiled layout (LAYOUT_TILED, cols % 512 == 0): the same bytes arranged in
       16-row x 128-column tiles (include/q4.h); the tensors here are flat.
     global_scale  NVFP4: float32 [1] (dequant multiplier); else None
+    FP8_ROW (W4A8 activations): codes uint8 [rows, cols] E4M3 (flat when
+      tiled), scales float32 [rows].
     """
     fmt: int
     rows: int
@@ -171,6 +174,11 @@ def empty_q4(fmt, rows: int, cols: int, device="cuda", layout=LAYOUT_ROWS) -> Q4
     """Allocate (with torch) the buffers of a quantized tensor."""
     f, lay = _fmt(fmt), _layout(layout)
     cb, sb = q4_sizes(f, rows, cols, lay)
+    if f == FP8_ROW:
+        codes = torch.empty((rows, cols) if lay == LAYOUT_ROWS else (cb,), dtype=torch.uint8,
+                            device=device)
+        return Q4Tensor(f, rows, cols, codes, torch.empty(rows, dtype=torch.float32, device=device),
+                        None, lay)
     g = GROUP[f]
     sdt = torch.int16 if f == INT4_G128 else torch.uint8
     if lay == LAYOUT_ROWS:
@@ -226,8 +234,8 @@ def q4_gemv(W: Q4Tensor, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch
 
 
 def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
-    """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16) or an MXFP4 Q4Tensor
-    (W4A4, with W MXFP4)."""
+    """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16), an MXFP4 Q4Tensor
+    (W4A4, with W MXFP4) or an FP8_ROW Q4Tensor (W4A8, with W INT4)."""
     wd = W.c()
     if isinstance(A, Q4Tensor):
         ad = A.c()

@@ -18,6 +18,7 @@ int block_of(int fmt) {
     case Q4_INT4_G128: return 128;
     case Q4_MXFP4: return 32;
     case Q4_NVFP4: return 16;
+    case Q4_FP8_ROW: return 16;  // row-major rows are stored in 16-byte pieces
     default: return 0;
   }
 }
@@ -78,7 +79,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int q4_version(void) { return 100; }
+int q4_version(void) { return 101; }
 
 const char* q4_status_string(int status) {
   switch (status) {
@@ -103,6 +104,11 @@ q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* code
   // the tiled layout stores whole 16-row tiles; per stored row both layouts
   // hold cols/2 code bytes and cols/g scales (fp16 for INT4)
   const size_t srows = layout == Q4_LAYOUT_TILED ? (size_t)((rows + 15) / 16) * 16 : (size_t)rows;
+  if (fmt == Q4_FP8_ROW) {  // one byte per value, one fp32 scale per row
+    if (codes_bytes) *codes_bytes = srows * (size_t)cols;
+    if (scales_bytes) *scales_bytes = (size_t)rows * 4;
+    return Q4_OK;
+  }
   if (codes_bytes) *codes_bytes = srows * (size_t)cols / 2;
   if (scales_bytes) *scales_bytes = srows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : 1);
   return Q4_OK;
@@ -117,6 +123,10 @@ q4_status q4_quantize(const void* src_bf16, int64_t ld, const q4_tensor* dst,
   st = check_bf16(src_bf16, dst->rows, dst->cols, ld);
   if (st != Q4_OK) return st;
   if (dst->fmt != Q4_NVFP4 && (dst->rows == 0 || dst->cols == 0)) return Q4_OK;
+  if (dst->fmt == Q4_FP8_ROW)
+    return hip_status(q4::launch_fp8_rows_quantize(dst->layout, static_cast<const uint16_t*>(src_bf16), ld,
+                                                   dst->rows, dst->cols, static_cast<uint8_t*>(dst->codes),
+                                                   static_cast<float*>(dst->scales), as_stream(stream)));
   return hip_status(q4::launch_quantize(
       dst->fmt, dst->layout, static_cast<const uint16_t*>(src_bf16), ld, dst->rows, dst->cols,
       static_cast<uint8_t*>(dst->codes), dst->scales, dst->global_scale, nv_global_in,
@@ -131,6 +141,10 @@ q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld,
   if (!dst) return Q4_ERR_NULL;
   if (ld < src->cols) return Q4_ERR_SHAPE;
   if (!aligned(dst, 16) || ld % (dst_dtype == 0 ? 8 : 4)) return Q4_ERR_ALIGN;
+  if (src->fmt == Q4_FP8_ROW)
+    return hip_status(q4::launch_fp8_rows_dequant(src->layout, static_cast<const uint8_t*>(src->codes),
+                                                  static_cast<const float*>(src->scales), src->rows,
+                                                  src->cols, dst, dst_dtype, ld, as_stream(stream)));
   return hip_status(q4::launch_dequant(src->fmt, src->layout, static_cast<const uint8_t*>(src->codes),
                                        src->scales, src->global_scale, src->rows, src->cols, dst,
                                        dst_dtype, ld, as_stream(stream)));
@@ -140,6 +154,7 @@ q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx
                   int64_t ldy, void* stream) {
   q4_status st = check_tensor(W);
   if (st != Q4_OK) return st;
+  if (W->fmt == Q4_FP8_ROW) return Q4_ERR_FORMAT;
   if (B < 0 || B > 16) return Q4_ERR_SHAPE;
   if (W->cols % 128) return Q4_ERR_SHAPE;
   if (B == 0 || W->rows == 0) return Q4_OK;
@@ -158,6 +173,7 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
                   const q4_tensor* W, void* C_bf16, int64_t ldc, void* stream) {
   q4_status st = check_tensor(W);
   if (st != Q4_OK) return st;
+  if (W->fmt == Q4_FP8_ROW) return Q4_ERR_FORMAT;
   if (M < 0 || M >= kMaxDim || M > (int64_t)65535 * 64) return Q4_ERR_SHAPE;
   if ((A_bf16 == nullptr) == (A_q == nullptr)) return A_bf16 ? Q4_ERR_FORMAT : Q4_ERR_NULL;
   const int64_t N = W->rows, K = W->cols;
@@ -165,7 +181,9 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
   if (A_q) {
     st = check_tensor(A_q);
     if (st != Q4_OK) return st;
-    if (A_q->fmt != Q4_MXFP4 || W->fmt != Q4_MXFP4) return Q4_ERR_FORMAT;
+    const bool w4a4 = A_q->fmt == Q4_MXFP4 && W->fmt == Q4_MXFP4;
+    const bool w4a8 = A_q->fmt == Q4_FP8_ROW && W->fmt == Q4_INT4_G128;
+    if (!w4a4 && !w4a8) return Q4_ERR_FORMAT;
     if (A_q->rows != M || A_q->cols != K) return Q4_ERR_SHAPE;
   }
   if (M == 0 || N == 0) return Q4_OK;
@@ -176,6 +194,11 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
   }
   st = check_out_bf16(C_bf16, M, N, ldc);
   if (st != Q4_OK) return st;
+  if (A_q && A_q->fmt == Q4_FP8_ROW)
+    return hip_status(q4::launch_gemm_w4a8(
+        A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const float*>(A_q->scales),
+        M, static_cast<const uint8_t*>(W->codes), static_cast<const uint16_t*>(W->scales), N, K,
+        static_cast<uint16_t*>(C_bf16), ldc, as_stream(stream)));
   if (A_q)
     return hip_status(q4::launch_gemm_w4a4(
         A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,
@@ -194,6 +217,7 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
                           void* stream) {
   q4_status st = check_tensor(W);
   if (st != Q4_OK) return st;
+  if (W->fmt == Q4_FP8_ROW) return Q4_ERR_FORMAT;
   if (E < 0 || E > 65535 || N < 0 || T < 0 || P < 0 || P >= kMaxDim || T >= kMaxDim)
     return Q4_ERR_SHAPE;
   if (W->rows != (int64_t)E * N) return Q4_ERR_SHAPE;

@@ -48,6 +48,21 @@ hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scale
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// Per-token FP8 (E4M3) quantization of bf16 src [rows][ld] into codes
+// (row-major [rows][cols] or the tiled FP8 layout) and fp32 scales [rows].
+hipError_t launch_fp8_rows_quantize(int layout, const uint16_t* src, int64_t ld, int64_t rows,
+                                    int64_t cols, uint8_t* codes, float* scales, hipStream_t stream);
+
+// FP8 rows -> row-major dst [rows][ld], dst_dtype 0 bf16 / 1 fp32.
+hipError_t launch_fp8_rows_dequant(int layout, const uint8_t* codes, const float* scales, int64_t rows,
+                                   int64_t cols, void* dst, int dst_dtype, int64_t ld, hipStream_t stream);
+
+// W4A8 GEMM C [M][ldc] = A8' . W'^T: A per-token FP8, W INT4 g128,
+// K % 128 == 0 (512 for a tiled operand).
+hipError_t launch_gemm_w4a8(int a_layout, int w_layout, const uint8_t* a_codes, const float* a_scales,
+                            int64_t M, const uint8_t* w_codes, const uint16_t* w_scales, int64_t N,
+                            int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
+
 // Grouped expert GEMM with the expert weights in the tiled layout (K % 512
 // == 0, N % 16 == 0, T > 0): the weight-streaming kernel of grouped.hip.
 hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather,

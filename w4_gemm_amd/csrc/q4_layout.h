@@ -51,6 +51,19 @@ __host__ __device__ __forceinline__ int64_t scale_off(int64_t r, int64_t k, int6
   }
 }
 
+// FP8 activations (per-row E4M3, the W4A8 operand), tiled layout: byte
+// offset of the operand dword holding the even (h = 0) or odd (h = 1)
+// elements of k0 .. k0 + 7 (k0 % 8 == 0) of row r.  Tiles of 16 rows x 128
+// k are 2048 bytes; lane l = 16g + n owns k = 32g .. 32g + 31 of row n as 32
+// operand bytes, operand dword 2w + h holding elements 32g + 8w + 2i + h
+// (i = 0..3, byte i); operand bytes 0..15 of all lanes come first, then
+// bytes 16..31.
+__host__ __device__ __forceinline__ int64_t fp8_tiled_dword(int64_t r, int64_t k0, int64_t K, int h) {
+  const int64_t S = K >> 7, t = r >> 4, n = r & 15, s = k0 >> 7;
+  const int g = (int)((k0 >> 5) & 3), w = (int)((k0 >> 3) & 3);
+  return ((t * S + s) << 11) + ((w >> 1) << 10) + ((g * 16 + n) << 4) + (((w & 1) * 2 + h) << 2);
+}
+
 // Rows of storage (the tiled layout pads the last tile to 16 rows).
 template <int LAYOUT>
 __host__ __device__ __forceinline__ int64_t stored_rows(int64_t rows) {

@@ -17,8 +17,9 @@ Recipe (the same for every workload):
 
 The five workloads are those of the benchmark: a small INT4 g128 GEMV, the
 MXFP4 decode GEMV (28672x8192), the NVFP4 prefill GEMM (4096x8192x8192), the
-MoE grouped expert GEMM (64 experts of 2048x7168, 256 tokens, top-8) and the
-W4A4 MXFP4 GEMM (8192^3).
+MoE grouped expert GEMM (64 experts of 2048x7168, 256 tokens, top-8), the
+W4A4 MXFP4 GEMM (8192^3) and the W4A8 GEMM (INT4 weights, per-token FP8
+activations, 4096x8192x8192).
 """
 from __future__ import annotations
 
@@ -167,6 +168,14 @@ def moe_grouped(seed: int = 0, experts: int = 64, n: int = 2048, k: int = 7168,
     return Workload("moe_grouped_mxfp4", "mxfp4", {"W": w, "A": a},
                     {"E": experts, "N": n, "K": k, "T": tokens, "topk": topk,
                      "routing": r, "logits": logits})
+
+
+def w4a8_gemm(seed: int = 0, m: int = 4096, n: int = 8192, k: int = 8192) -> Workload:
+    """W4A8 prefill, the prefill shape: A ~ N(0, 1) with 1% of channels x10
+    (per-token FP8), W ~ N(0, 0.02^2) (INT4 g128)."""
+    a = matrix("w4a8/A", m, k, 1.0, seed, channel_frac=0.01, channel_mult=10.0)
+    w = matrix("w4a8/W", n, k, 0.02, seed)
+    return Workload("w4a8_int4_fp8_gemm", "int4", {"A": a, "W": w}, {"M": m, "N": n, "K": k})
 
 
 def w4a4_gemm(seed: int = 0, m: int = 8192, n: int = 8192, k: int = 8192) -> Workload:
