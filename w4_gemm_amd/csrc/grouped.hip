@@ -11,27 +11,32 @@
 // in LDS.
 //
 // Work decomposition:
-//   * a workgroup of 8 waves covers 512 weight rows of one expert (grid.y =
-//     expert); wave w streams four adjacent 16-row tiles over the whole K,
-//     so every activation fragment read from LDS feeds four matrix
-//     instructions (fragment traffic into registers, not HBM, was what held
-//     the first version back).
+//   * a workgroup of 8 waves covers 256 weight rows of one expert (grid.y =
+//     expert); wave w owns two adjacent 16-row tiles over the whole K, so
+//     every activation fragment read from LDS feeds two matrix instructions.
+//     A workgroup needs 74 KB of LDS and ~100 registers per lane, so two
+//     run on each CU (16 waves) and one's barrier waits overlap the other's
+//     streaming.
 //   * the expert's routed rows are taken in chunks of 48 (three batch tiles
 //     of 16; a chunk with fewer rows skips the empty batch tiles -- the MoE
 //     workload has 17..46 rows per expert, one chunk each).
-//   * K advances in steps of 256 (2 super-chunks): the chunk's activation
-//     rows for the step (48 x 256 bf16) are gathered into LDS by the whole
-//     workgroup (two buffers), and each wave's weight codes and scales for
-//     the next step are loaded into registers while the current step is
-//     multiplied -- 8 KB in flight per wave.  Issue order is pinned (next x,
-//     next weights, then math) so the x wait never waits for the weights.
+//   * K advances in stages of one super-chunk (128 k).  The weight tiles of
+//     a stage (16 x 1 KB) are copied verbatim into LDS by direct global->LDS
+//     loads (each wave its own two tiles), two stages ahead, into a ring of
+//     three buffers; with two workgroups per CU, 64 KB of weights per CU
+//     stay in flight without holding registers.  Scale words (one group of
+//     four stages) are loaded into registers ahead of their group.  The
+//     chunk's activation rows for a stage (48 x 128 bf16) are gathered into
+//     LDS through registers by waves 0..5 (two buffers).
+//   * one barrier per stage; every wait is an explicit vmcnt count (the
+//     stage loop is unrolled by four so each count is a constant).
 //   * matrix step i of a super-chunk uses codes 8i..8i+8 of every lane of a
 //     weight tile (k = 32g + 8i + [0,8) for lane 16g + n); the activation
 //     fragment is read for the same k.  Weights are the row operand of
 //     v_mfma_f32_16x16x32_bf16, so a lane ends with 4 consecutive columns of
 //     one routed row: 8-byte stores.
-//   * rows whose gather index is outside [0, T) are staged as zeros and so
-//     produce zero output rows.
+//   * a row whose gather index is outside [0, T) is staged from row 0 and its
+//     output row written as zeros.
 #include "q4_launch.h"
 #include "q4_layout.h"
 #include "q4_mma.h"
@@ -40,25 +45,49 @@ namespace q4 {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kTPW = 4;                 // weight tiles per wave
-constexpr int kRows = 48;               // routed rows per chunk
-constexpr int kSCS = 2;                 // super-chunks per step
-constexpr int kStepK = 128 * kSCS;      // 256
-constexpr int kXRow = kStepK + 8;       // padded LDS row (bf16)
-constexpr int kBT = kRows / 16;                         // batch tiles per chunk
-constexpr int kPPR = kStepK / 8;                        // 16-byte pieces per row and step
-constexpr int kXPer = kRows * kPPR / (kWaves * 64);     // pieces per thread and step
-constexpr int kRowStride = kWaves * 64 / kPPR;          // rows between a thread's pieces
-constexpr size_t kSmemBytes = 2ull * kRows * kXRow * 2;
-static_assert(kSCS == 1 || kSCS == 2 || kSCS == 4, "a step lies within one scale group");
-static_assert(kRows % 16 == 0 && kRows * kPPR % (kWaves * 64) == 0, "staging split");
+constexpr int kTPW = 2;                    // weight tiles per wave
+constexpr int kTiles = kWaves * kTPW;      // 16 tiles = 256 weight rows per workgroup
+constexpr int kRows = 48;                  // routed rows per chunk
+constexpr int kBT = kRows / 16;            // batch tiles per chunk
+constexpr int kWBufs = 3;                  // weight stages in LDS (2 in flight)
+constexpr int kXRow = 128 + 8;             // padded LDS row of one stage's activations (bf16)
+constexpr int kXThreads = kRows * 16 / 2;  // threads staging activations, 2 pieces each (384)
+constexpr size_t kWBytes = (size_t)kWBufs * kTiles * 1024;               // 48 KB
+constexpr size_t kSmemBytes = kWBytes + 2ull * kRows * kXRow * 2;        // + 25.5 KB
+static_assert(kXThreads % 64 == 0 && kXThreads <= kWaves * 64, "staging split");
 
-// codes and raw scale words of one step of one weight tile
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// raw scale words of one weight tile for one group of four super-chunks
 template <int FMT>
-struct StepW {
-  static constexpr int NSW = FMT == 1 ? 1 : 2;  // words per tile and scale group
-  u32x4_t w[kSCS];
-  uint32_t sw[NSW];
+struct ScaleW {
+  static constexpr int NSW = FMT == 1 ? 1 : 2;
+  uint32_t w[NSW];
 };
 
 template <int FMT>
@@ -68,8 +97,9 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
                      const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                      const float* __restrict__ gs_ptr, int N, int K, uint16_t* __restrict__ C,
                      int64_t ldc) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs_raw[];
-  auto xs = reinterpret_cast<uint16_t(*)[kRows][kXRow]>(xs_raw);
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  uint8_t (*wbuf)[kTiles][1024] = reinterpret_cast<uint8_t (*)[kTiles][1024]>(smem);
+  auto xs = reinterpret_cast<uint16_t(*)[kRows][kXRow]>(smem + kWBytes);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,65 +109,70 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
   if (r0 >= r1) return;  // whole workgroup, before any barrier
 
   const int NT = N >> 4;                     // weight tiles per expert (N % 16 == 0)
-  const int S = K >> 7, Q = K >> 9, nst = K / kStepK;
-  const int tile0 = blockIdx.x * (kWaves * kTPW) + wave * kTPW;  // within the expert
+  const int S = K >> 7, Q = K >> 9;
+  const int tile0 = blockIdx.x * kTiles + wave * kTPW;  // within the expert
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
 
-  // this lane's code bytes and scale words of super-chunk 0 / scale group 0
+  // wave-uniform code base of each of the wave's tiles; per-lane scale words
   const uint8_t* wsrc[kTPW];
   const uint8_t* ssrc[kTPW];
 #pragma unroll
   for (int t = 0; t < kTPW; ++t) {
     const int64_t gt = (int64_t)e * NT + min(tile0 + t, NT - 1);
-    wsrc[t] = codes + gt * S * 1024 + lane * 16;
+    wsrc[t] = codes + gt * S * 1024;
     if constexpr (FMT == 0) ssrc[t] = scales + (gt * Q * 16 + (lane & 15)) * 8;
     else if constexpr (FMT == 1) ssrc[t] = scales + (gt * Q * 64 + lane) * 4;
     else ssrc[t] = scales + (gt * Q * 64 + lane) * 8;
   }
-  // step st covers super-chunks kSCS*st .. +kSCS, all in scale group
-  // kSCS*st/4 (the codes' position in the group: (kSCS*st) % 4 + c)
-  auto load_w = [&](StepW<FMT> (&f)[kTPW], int st) {
-    const int q = min(kSCS * st / 4, Q - 1);
+  auto issue_w = [&](int st) {  // stage st (clamped) into ring slot st % kWBufs
+    const int sc = min(st, S - 1);
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t)
+      copy16_to_lds(uniform_ptr(wsrc[t] + (int64_t)sc * 1024) + lane * 16, wbuf[st % kWBufs][wave * kTPW + t]);
+  };
+  ScaleW<FMT> snext[kTPW], scur[kTPW];
+  auto issue_s = [&](int q) {
+    q = min(q, Q - 1);
 #pragma unroll
     for (int t = 0; t < kTPW; ++t) {
-#pragma unroll
-      for (int c = 0; c < kSCS; ++c)
-        f[t].w[c] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(wsrc[t] + (int64_t)min(kSCS * st + c, S - 1) * 1024));
       if constexpr (FMT == 1) {
-        f[t].sw[0] = *reinterpret_cast<const uint32_t*>(ssrc[t] + (int64_t)q * 256);
+        snext[t].w[0] = *reinterpret_cast<const uint32_t*>(ssrc[t] + (int64_t)q * 256);
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(ssrc[t] + (int64_t)q * (FMT == 0 ? 128 : 512));
-        f[t].sw[0] = v.x;
-        f[t].sw[1] = v.y;
+        snext[t].w[0] = v.x;
+        snext[t].w[1] = v.y;
       }
     }
   };
+  constexpr int kSLoads = kTPW;  // one scale load instruction per tile
+
+  const bool xw = tid < kXThreads;           // waves 0..5 stage activations
+  const int xrow = (tid >> 4) % kRows;       // this thread's two rows: xrow, xrow + 24
+  const int xk = (tid & 15) * 8;             // its 8 k within a stage
 
   for (int c0 = r0; c0 < r1; c0 += kRows) {
     const int nb = min(kBT, (r1 - c0 + 15) >> 4);  // batch tiles with rows
-    // the rows this thread stages: row tid/kPPR + kRowStride*j, source or -1
-    const int trow = tid / kPPR;
-    int srow[kXPer];
+    int srow[2];
 #pragma unroll
-    for (int j = 0; j < kXPer; ++j) {
-      const int p = c0 + trow + kRowStride * j;
+    for (int j = 0; j < 2; ++j) {
+      const int p = c0 + xrow + 24 * j;
       const int g = p < r1 ? gather[p] : -1;
-      srow[j] = (g >= 0 && g < T) ? g : -1;
+      srow[j] = (g >= 0 && g < T) ? g : 0;  // invalid rows staged from row 0, output zeroed
     }
-    const int xk = (tid % kPPR) * 8;  // this thread's 8 k within a step
-    u32x4_t xr[kXPer];
+    u32x4_t xr[2];
     auto load_x = [&](int st) {
-      const int k = min(st * kStepK + xk, K - 8);
+      if (xw) {
+        const int k = min(st, S - 1) * 128 + xk;
 #pragma unroll
-      for (int j = 0; j < kXPer; ++j)
-        xr[j] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)max(srow[j], 0) * lda + k);
+        for (int j = 0; j < 2; ++j)
+          xr[j] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)srow[j] * lda + k);
+      }
     };
     auto store_x = [&](int buf) {
+      if (xw) {
 #pragma unroll
-      for (int j = 0; j < kXPer; ++j)
-        *reinterpret_cast<u32x4_t*>(&xs[buf][trow + kRowStride * j][xk]) =
-            srow[j] >= 0 ? xr[j] : u32x4_t{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&xs[buf][xrow + 24 * j][xk]) = xr[j];
+      }
     };
 
     f32x4_t acc[kTPW][kBT];
@@ -146,72 +181,85 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
 #pragma unroll
       for (int bt = 0; bt < kBT; ++bt) acc[t][bt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto step_math = [&](const StepW<FMT> (&f)[kTPW], int buf, int st) {
-      const uint16_t* xb = &xs[buf][lane & 15][32 * (lane >> 4)];
-      const int cq0 = (kSCS * st) & 3;  // position of super-chunk 0 of the step in its group
+    // math of stage st; j = st % 4 is its position in the scale group
+    auto stage_math = [&](int st, auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const uint16_t* xb = &xs[st & 1][lane & 15][32 * (lane >> 4)];
+      u32x4_t wv[kTPW];
 #pragma unroll
-      for (int c = 0; c < kSCS; ++c) {
-        const int cq = cq0 + c;
+      for (int t = 0; t < kTPW; ++t)
+        wv[t] = *reinterpret_cast<const u32x4_t*>(&wbuf[st % kWBufs][wave * kTPW + t][lane * 16]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bf16x8_t wb[kTPW];
+      for (int i = 0; i < 4; ++i) {
+        bf16x8_t wb[kTPW];
 #pragma unroll
-          for (int t = 0; t < kTPW; ++t) {
-            if constexpr (FMT == 0) {
-              const uint32_t h = (f[t].sw[cq >> 1] >> (16 * (cq & 1))) & 0xFFFFu;
-              wb[t] = dq8_int4(f[t].w[c][i], fp16_value(h));
-            } else if constexpr (FMT == 1) {
-              wb[t] = dq8_e2m1(f[t].w[c][i], e8m0_value((f[t].sw[0] >> (8 * cq)) & 0xFFu));
-            } else {
-              const uint32_t sb = (f[t].sw[cq >> 1] >> (16 * (cq & 1) + 8 * (i >> 1))) & 0xFFu;
-              wb[t] = dq8_e2m1_mul(f[t].w[c][i], e4m3_value(sb) * gs);
-            }
+        for (int t = 0; t < kTPW; ++t) {
+          if constexpr (FMT == 0) {
+            const uint32_t h = (scur[t].w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            wb[t] = dq8_int4(wv[t][i], fp16_value(h));
+          } else if constexpr (FMT == 1) {
+            wb[t] = dq8_e2m1(wv[t][i], e8m0_value((scur[t].w[0] >> (8 * j)) & 0xFFu));
+          } else {
+            const uint32_t sb = (scur[t].w[j >> 1] >> (16 * (j & 1) + 8 * (i >> 1))) & 0xFFu;
+            wb[t] = dq8_e2m1_mul(wv[t][i], e4m3_value(sb) * gs);
           }
+        }
 #pragma unroll
-          for (int bt = 0; bt < kBT; ++bt) {
-            if (bt < nb) {
-              const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xb + bt * 16 * kXRow + c * 128 + 8 * i));
+        for (int bt = 0; bt < kBT; ++bt) {
+          if (bt < nb) {
+            const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(xb + bt * 16 * kXRow + 8 * i));
 #pragma unroll
-              for (int t = 0; t < kTPW; ++t) acc[t][bt] = mma16x16x32(wb[t], a, acc[t][bt]);
-            }
+            for (int t = 0; t < kTPW; ++t) acc[t][bt] = mma16x16x32(wb[t], a, acc[t][bt]);
           }
         }
       }
     };
 
-    // Pinned issue order: next x, then next weights, then the math.
-    StepW<FMT> fa[kTPW], fb[kTPW];
-    auto prefetch = [&](StepW<FMT> (&f)[kTPW], int st) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_x(st);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(f, st);
-      __builtin_amdgcn_sched_barrier(0);
-    };
+    // Copy plan, per iteration st (j = st % 4): x(st+1) loads, the weight
+    // DMA of stage st+2 (kTPW per wave), and when j == 2 the scale words of
+    // group st/4 + 1 (kTPW loads, after W(st+2) = the group's first stage).
+    // At the top of iteration st, W(st) -- and at j == 0 the scales of the
+    // group -- must have landed; the copies issued after them may stay in
+    // flight: W(st+1), plus at j == 3 the scale loads issued after it.
+    // Prologue: x(0), W(0), scales(0), W(1).
     load_x(0);
-    load_w(fa, 0);
+    issue_w(0);
+    issue_s(0);
+    issue_w(1);
+    wait_vmcnt<2 * kTPW + kSLoads>();  // x(0) landed (W(0..2) and scales may not have)
     store_x(0);
-    __syncthreads();
-    int st = 0;
-    for (; st + 2 < nst; st += 2) {
-      prefetch(fb, st + 1);
-      step_math(fa, st & 1, st);
+    auto iteration = [&](int st, auto jc) {
+      constexpr int J = decltype(jc)::value;
+      if constexpr (J == 3) wait_vmcnt<kTPW + kSLoads>();
+      else wait_vmcnt<kTPW>();
+      stage_barrier();
+      if constexpr (J == 0) {
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t) scur[t] = snext[t];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(st + 1);
+      issue_w(st + 2);
+      if constexpr (J == 2) issue_s((st >> 2) + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_math(st, jc);
+      // x(st+1) has landed once at most the copies issued after it remain
+      if constexpr (J == 2) wait_vmcnt<kTPW + kSLoads>();
+      else wait_vmcnt<kTPW>();
       store_x((st + 1) & 1);
-      __syncthreads();
-      prefetch(fa, st + 2);
-      step_math(fb, (st + 1) & 1, st + 1);
-      store_x(st & 1);
-      __syncthreads();
+    };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
+    // K % 512 == 0 in the tiled layout: S is a multiple of 4
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      iteration(s0, J0());
+      iteration(s0 + 1, J1());
+      iteration(s0 + 2, J2());
+      iteration(s0 + 3, J3());
     }
-    if (st + 1 < nst) {  // two steps left
-      prefetch(fb, st + 1);
-      step_math(fa, st & 1, st);
-      store_x((st + 1) & 1);
-      __syncthreads();
-      step_math(fb, (st + 1) & 1, st + 1);
-    } else {             // one step left
-      step_math(fa, st & 1, st);
-    }
+    wait_vmcnt<0>();
 
     // tile t, batch tile bt: lane l, register q holds C[p][n] with
     // p = c0 + 16bt + l%16 and n = 16(tile0+t) + 4(l/16) + q
@@ -223,13 +271,14 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
         for (int bt = 0; bt < kBT; ++bt) {
           const int p = c0 + 16 * bt + (lane & 15);
           if (bt < nb && p < r1) {
-            const f32x4_t v = acc[t][bt];
+            const int g = gather[p];
+            const f32x4_t v = (g >= 0 && g < T) ? acc[t][bt] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             *reinterpret_cast<uint2*>(C + (int64_t)p * ldc + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
           }
         }
       }
     }
-    __syncthreads();  // the next chunk reuses the LDS buffers
+    stage_barrier();  // the next chunk reuses the LDS buffers
   }
 }
 
