@@ -20,6 +20,10 @@ definitions in fp64 on the oracle's own dequantized weights:
   * Grouped MoE GEMM: one low-bit weight matrix per expert, each routed row
     multiplied by its expert's matrix (same page, "A few details", MoE
     grouped GEMM bullet).
+  * The MoE layer around it: top-k routing with softmax gates, SwiGLU
+    expert FFN (gate/up grouped GEMM, silu(gate) * up, down grouped GEMM)
+    and the gated combine -- plain definitions in fp64 (readings stated in
+    the functions).
 
 numpy's fp64 matmul is the only library primitive used as a step.
 """
@@ -331,6 +335,98 @@ def gemm_w4a8(a, q: QTensor, rows=None, aq: FP8Rows | None = None) -> np.ndarray
         r = np.asarray(rows)
         aq = FP8Rows(len(r), aq.cols, aq.codes[r], aq.scales[r])
     return matmul_f64(dequant_fp8_rows(aq), dequant(q))
+
+
+# --------------------------------------------------------------------------
+# MoE layer around the grouped GEMM (routing, SwiGLU, combine)
+# --------------------------------------------------------------------------
+class Routing:
+    """Top-k routing of T tokens over E experts: ids/weights [T, k] (choice j
+    = j-th largest logit, ties to the lower expert id), expert offsets [E+1],
+    gather [T*k] (token of each routed row; rows expert-major, tokens
+    ascending within an expert) and inv [T, k] (routed row of each choice)."""
+
+    def __init__(self, ids, weights, offsets, gather, inv):
+        self.ids, self.weights, self.offsets, self.gather, self.inv = ids, weights, offsets, gather, inv
+
+
+def moe_route(logits, k: int) -> Routing:
+    """Routing for one MoE layer: each token goes to the k experts with the
+    largest router logits (ties to the lower expert id); its gate for a
+    chosen expert is that expert's softmax probability over all E logits
+    (fp64), not renormalized over the k.  Rows are then grouped by expert
+    ("Low-bit inference for very large MoE", "A few details": one low-bit
+    matrix per expert, tokens grouped by routing)."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.zeros((T, k), dtype=np.int32)
+    weights = np.zeros((T, k), dtype=np.float64)
+    l64 = lg.astype(np.float64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))
+        ids[t] = order[:k]
+        z = np.exp(l64[t] - l64[t].max())
+        p = z / z.sum()
+        weights[t] = p[ids[t]]
+    counts = np.bincount(ids.ravel(), minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    gather = np.zeros(T * k, dtype=np.int32)
+    inv = np.zeros((T, k), dtype=np.int32)
+    nxt = offsets[:-1].copy()
+    for t in range(T):          # tokens ascending: stable within each expert
+        for e in sorted(ids[t]):
+            j = int(np.where(ids[t] == e)[0][0])
+            gather[nxt[e]] = t
+            inv[t, j] = nxt[e]
+            nxt[e] += 1
+    return Routing(ids, weights, offsets, gather, inv)
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(gu, inter: int) -> np.ndarray:
+    """SwiGLU of a gate/up product row: h = silu(gate) * up, where gate is
+    columns [0, inter) and up columns [inter, 2*inter) of gu (fp64)."""
+    gu = np.asarray(gu, dtype=np.float64)
+    return silu(gu[:, :inter]) * gu[:, inter:2 * inter]
+
+
+def moe_combine(y, inv, weights) -> np.ndarray:
+    """out[t] = sum_j weights[t, j] * y[inv[t, j]] (fp64)."""
+    y = np.asarray(y, dtype=np.float64)
+    inv = np.asarray(inv)
+    w = np.asarray(weights, dtype=np.float64)
+    return np.einsum("tj,tjn->tn", w, y[inv])
+
+
+def moe_layer(x, logits, k: int, q_gu: QTensor, q_down: QTensor, inter: int, tokens=None):
+    """One MoE FFN layer in fp64 on the oracle's dequantized weights:
+    out[t] = sum_j g_tj * W_down_e (silu(W_gate_e x_t) * (W_up_e x_t)),
+    e = the token's j-th expert, with W_gu_e = [W_gate_e; W_up_e] rows
+    [e*2I, (e+1)*2I) of q_gu and W_down_e rows [e*K, (e+1)*K) of q_down.
+    Returns (out [len(tokens), K], Routing)."""
+    x = np.asarray(x, dtype=np.float32)
+    r = moe_route(logits, k)
+    K = x.shape[1]
+    tokens = range(x.shape[0]) if tokens is None else tokens
+    out = np.zeros((len(tokens), K), dtype=np.float64)
+    cache = {}
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            e = int(r.ids[t, j])
+            if e not in cache:
+                cache[e] = (dequant_rows(q_gu, np.arange(e * 2 * inter, (e + 1) * 2 * inter)).astype(np.float64),
+                            dequant_rows(q_down, np.arange(e * K, (e + 1) * K)).astype(np.float64))
+            wgu, wd = cache[e]
+            gu = wgu @ x[t].astype(np.float64)
+            h = silu(gu[:inter]) * gu[inter:]
+            out[i] += r.weights[t, j] * (wd @ h)
+    return out, r
 
 
 def grouped_gemm(a, gather, offsets, q_all: QTensor, n: int, experts=None) -> np.ndarray:
