@@ -260,6 +260,8 @@ def main():
         extra["moe_grouped_mxfp4_64x2048x7168"] = bench_moe(torch, q4, workloads, dev, args.seed)
     if want("w4a4"):
         extra["w4a4_mxfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed)
+    if want("moe_layer"):
+        extra["moe_layer_mxfp4_64x(2x2048|7168)"] = bench_moe_layer(torch, q4, workloads, dev, args.seed)
     if want("w4a8"):
         extra["w4a8_int4_fp8_gemm_4096x8192x8192"] = bench_w4a8(torch, q4, workloads, dev, args.seed)
 
@@ -344,6 +346,56 @@ def bench_moe(torch, q4, workloads, dev, seed):
             "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2), "routed_rows": P,
             "rows_per_expert_min_max": [int(min(r.offsets[1:] - r.offsets[:-1])),
                                         int(max(r.offsets[1:] - r.offsets[:-1]))]}
+
+
+def bench_moe_layer(torch, q4, workloads, dev, seed):
+    """The MoE FFN layer at the MoE workload's shapes: route -> gate/up
+    grouped GEMM (64 x 4096 x 7168) -> SwiGLU -> down grouped GEMM (64 x
+    7168 x 2048) -> combine, 256 tokens, top-8, MXFP4 tiled weights.  The
+    weights (2.8 G values) are drawn on the GPU (torch generator seeded with
+    `seed`, N(0, 0.02^2)) -- drawing them on the host takes minutes; x and
+    the router logits are the MoE workload's."""
+    log("generating the MoE layer workload (64 experts, gate/up 4096x7168, down 7168x2048)")
+    E, I, K, T, k = 64, 2048, 7168, 256, 8
+    g = torch.Generator(device=dev).manual_seed(seed)
+    w = (torch.randn((E * 2 * I, K), generator=g, device=dev) * 0.02).bfloat16()
+    qgu = q4.quantize(w, "mxfp4", layout="tiled")
+    del w
+    w = (torch.randn((E * K, I), generator=g, device=dev) * 0.02).bfloat16()
+    qd = q4.quantize(w, "mxfp4", layout="tiled")
+    del w
+    torch.cuda.empty_cache()
+    x = workloads.matrix("moe/A", T, K, 1.0, seed).to(dev)
+    logits = torch.from_numpy(workloads.normal_f32("moe/logits", T * E, seed).reshape(T, E)).to(dev)
+    P = T * k
+    r = q4.q4_moe_route(logits, k)
+    gu = torch.empty((P, 2 * I), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((P, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((P, K), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    L = q4.lib()
+    steps = {
+        "route": lambda: q4.q4_moe_route(logits, k),
+        "gate_up": lambda: q4.q4_grouped_gemm(x, r.gather, r.offsets, qgu, 2 * I, gu),
+        "swiglu": lambda: q4.q4_swiglu(gu, I, h),
+        "down": lambda: q4.q4_grouped_gemm(h, None, r.offsets, qd, K, y),
+        "combine": lambda: q4.q4_moe_combine(y, r, out),
+    }
+
+    def layer():
+        q4._check(L.q4_moe_route(q4._ptr(logits), E, T, E, k, q4._ptr(r.ids), q4._ptr(r.weights),
+                                 q4._ptr(r.offsets), q4._ptr(r.gather), q4._ptr(r.inv), q4._stream(None)),
+                  "q4_moe_route")
+        for name in ("gate_up", "swiglu", "down", "combine"):
+            steps[name]()
+
+    ms = timed(torch, layer, 10, 2)
+    per = {n: round(timed(torch, f, 10, 2) * 1e3, 1) for n, f in steps.items()}
+    wbytes = qgu.nbytes + qd.nbytes
+    return {"us": round(ms * 1e3, 1), "weight_bytes": wbytes,
+            "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "steps_us": per, "tokens": T, "topk": k}
 
 
 def bench_w4a4(torch, q4, workloads, dev, seed):

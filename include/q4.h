@@ -206,7 +206,8 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
  * e owns rows [e*N, (e+1)*N).  For every expert e and every routed row p in
  * [expert_offsets[e], expert_offsets[e+1]):
  *     C[p][n] = sum_k A[gather[p]][k] * w'[e*N + n][k]
- * A_bf16 [T][lda] (T tokens), gather int32 [P] (device), expert_offsets
+ * A_bf16 [T][lda] (T tokens), gather int32 [P] (device; NULL means the
+ * identity, row p reads A[p], and needs T >= P), expert_offsets
  * int32 [E+1] (device, non-decreasing, offsets[0] = 0, offsets[E] = P),
  * C_bf16 [P][ldc].  The kernels read the offsets on the device (no host
  * sync) and clamp every range to [0, P]; a row whose gather index is outside
@@ -216,6 +217,49 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
                           const int32_t* expert_offsets, int32_t E, int64_t P,
                           const q4_tensor* W, int64_t N, void* C_bf16, int64_t ldc,
                           void* stream);
+
+/*
+ * The steps of an MoE layer around q4_grouped_gemm ("Low-bit inference for
+ * very large MoE", "A few details": one low-bit matrix per expert, tokens
+ * grouped by routing).  A layer is
+ *   q4_moe_route -> q4_grouped_gemm (gate/up: W rows [e*2I, (e+1)*2I) =
+ *   [W_gate_e; W_up_e]) -> q4_swiglu -> q4_grouped_gemm (down: gather =
+ *   0..P-1, W rows [e*K, (e+1)*K)) -> q4_moe_combine.
+ */
+
+/*
+ * Routing of T tokens over E experts from fp32 router logits [T][ld].
+ * Token t's experts are its k largest logits, largest first, ties to the
+ * lower expert id: topk_ids [T][k]; its gate for each is that expert's
+ * softmax probability over all E logits (fp32, not renormalized):
+ * topk_weights [T][k].  Routed rows are ordered expert-major and, within an
+ * expert, by token: expert_offsets [E+1], gather [T*k] (token of each row)
+ * and inv [T][k] (row of each choice).  All int32/fp32 device arrays, 4-byte
+ * aligned.  1 <= E <= 1024, 1 <= k <= min(E, 32), and the dispatch runs in
+ * one workgroup whose LDS holds a token bitmap per expert:
+ * 8*E*(ceil(T/32) + 1) bytes <= 160 KB (E = 64: T <= 10208), else
+ * Q4_ERR_SHAPE.  T == 0 writes expert_offsets = 0.
+ */
+q4_status q4_moe_route(const float* logits, int64_t ld, int64_t T, int32_t E, int32_t k,
+                       int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                       int32_t* gather, int32_t* inv, void* stream);
+
+/*
+ * SwiGLU between the expert GEMMs: h[p][n] = bf16(silu(g) * u), g =
+ * gu[p][n], u = gu[p][I + n], silu(z) = z / (1 + exp(-z)), fp32 math.
+ * gu_bf16 [P][ld_gu] (ld_gu >= 2I), h_bf16 [P][ldh]; I % 8 == 0.
+ */
+q4_status q4_swiglu(const void* gu_bf16, int64_t ld_gu, int64_t P, int64_t I, void* h_bf16,
+                    int64_t ldh, void* stream);
+
+/*
+ * Gated combine: out[t][n] = bf16(sum_j weights[t][j] * y[inv[t][j]][n]),
+ * fp32 accumulation in choice order.  y_bf16 [P][ldy] (expert outputs in
+ * routed-row order), inv/weights [T][k] as q4_moe_route writes them,
+ * out_bf16 [T][ldo]; N % 8 == 0.
+ */
+q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, const float* weights,
+                         int64_t T, int32_t k, int64_t N, void* out_bf16, int64_t ldo, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_grouped_gemm"):
+    for n in ("q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_grouped_gemm",
+              "q4_moe_route", "q4_swiglu", "q4_moe_combine"):
         assert n in names
 
 
@@ -170,7 +171,7 @@ def test_grouped_validation():
 
     assert call(N=100) == SHAPE                  # W rows != E*N
     assert call(E=-1) == SHAPE
-    assert call(gather=None) == NULL
+    assert call(gather=None) == SHAPE          # identity gather needs T >= P
     assert call(off=None) == NULL
     assert call(gather=A16 + 2) == ALIGN
     assert call(lda=500) == SHAPE
@@ -178,3 +179,28 @@ def test_grouped_validation():
     assert call(P=0) == OK
     assert call(W=desc(rows=8 * 128, cols=96), N=128) == SHAPE
     assert call(W=desc(rows=8 * 120, cols=512, layout=1), N=120) == SHAPE  # tiled: N % 16
+
+
+def test_moe_validation():
+    L = q4.lib()
+    B = A16
+    # q4_moe_route(logits, ld, T, E, k, ids, weights, offsets, gather, inv, stream)
+    assert L.q4_moe_route(B, 64, 256, 64, 0, B, B, B, B, B, None) == SHAPE
+    assert L.q4_moe_route(B, 64, 256, 64, 65, B, B, B, B, B, None) == SHAPE
+    assert L.q4_moe_route(B, 64, 256, 4, 8, B, B, B, B, B, None) == SHAPE      # k > E
+    assert L.q4_moe_route(B, 2048, 256, 2048, 8, B, B, B, B, B, None) == SHAPE  # E > 1024
+    assert L.q4_moe_route(B, 64, 20000, 64, 8, B, B, B, B, B, None) == SHAPE    # dispatch LDS
+    assert L.q4_moe_route(B, 32, 256, 64, 8, B, B, B, B, B, None) == SHAPE      # ld < E
+    assert L.q4_moe_route(None, 64, 256, 64, 8, B, B, B, B, B, None) == NULL
+    assert L.q4_moe_route(B, 64, 256, 64, 8, B, B, None, B, B, None) == NULL
+    assert L.q4_moe_route(B, 64, 256, 64, 8, B, B, B + 2, B, B, None) == ALIGN
+    # q4_swiglu(gu, ld_gu, P, I, h, ldh, stream)
+    assert L.q4_swiglu(B, 64, 8, 20, B, 32, None) == SHAPE                       # I % 8
+    assert L.q4_swiglu(B, 60, 8, 32, B, 32, None) == SHAPE                       # ld_gu < 2I
+    assert L.q4_swiglu(None, 64, 8, 32, B, 32, None) == NULL
+    assert L.q4_swiglu(B, 64, 0, 32, B, 32, None) == OK
+    # q4_moe_combine(y, ldy, inv, w, T, k, N, out, ldo, stream)
+    assert L.q4_moe_combine(B, 64, B, B, 4, 2, 60, B, 64, None) == SHAPE          # N % 8
+    assert L.q4_moe_combine(B, 64, B, B, 4, 0, 64, B, 64, None) == SHAPE
+    assert L.q4_moe_combine(B, 64, None, B, 4, 2, 64, B, 64, None) == NULL
+    assert L.q4_moe_combine(B, 64, B, B, 0, 2, 64, B, 64, None) == OK

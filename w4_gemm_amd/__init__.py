@@ -21,7 +21,8 @@ __all__ = [
     "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
-    "q4_grouped_gemm", "empty_q4", "quantize", "LIB_PATH",
+    "q4_grouped_gemm", "q4_moe_route", "q4_swiglu", "q4_moe_combine", "moe_layer",
+    "empty_q4", "quantize", "LIB_PATH",
 ]
 
 INT4_G128, MXFP4, NVFP4, FP8_ROW = 0, 1, 2, 3
@@ -80,6 +81,9 @@ def _lib_handle():
             "q4_gemm": ([i64, vp, i64, P, P, vp, i64, vp], ctypes.c_int),
             "q4_grouped_gemm": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
                                 ctypes.c_int),
+            "q4_moe_route": ([vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "q4_swiglu": ([vp, i64, i64, i64, vp, i64, vp], ctypes.c_int),
+            "q4_moe_combine": ([vp, i64, vp, vp, i64, i32, i64, vp, i64, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -251,12 +255,81 @@ def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
 def q4_grouped_gemm(A: torch.Tensor, gather: torch.Tensor, offsets: torch.Tensor, W: Q4Tensor,
                     N: int, C: torch.Tensor, stream=None) -> torch.Tensor:
     """For expert e, rows p in [offsets[e], offsets[e+1]):
-    C[p] = A[gather[p]] . w'_e^T, with W stacked expert-major (E*N rows)."""
-    if gather.dtype != torch.int32 or offsets.dtype != torch.int32:
+    C[p] = A[gather[p]] . w'_e^T, with W stacked expert-major (E*N rows).
+    gather None: row p reads A[p] (P = C.shape[0] rows)."""
+    if (gather is not None and gather.dtype != torch.int32) or offsets.dtype != torch.int32:
         raise ValueError("gather and offsets must be int32")
     E = offsets.numel() - 1
+    P = C.shape[0] if gather is None else gather.numel()
     wd = W.c()
     _check(lib().q4_grouped_gemm(_ptr(A), A.stride(0), A.shape[0], _ptr(gather), _ptr(offsets),
-                                 E, gather.numel(), ctypes.byref(wd), N, _ptr(C), C.stride(0),
+                                 E, P, ctypes.byref(wd), N, _ptr(C), C.stride(0),
                                  _stream(stream)), "q4_grouped_gemm")
     return C
+
+
+@dataclass
+class Routing:
+    """Device tensors written by q4_moe_route (see include/q4.h)."""
+    ids: torch.Tensor        # int32 [T, k]
+    weights: torch.Tensor    # float32 [T, k]
+    offsets: torch.Tensor    # int32 [E + 1]
+    gather: torch.Tensor     # int32 [T * k]
+    inv: torch.Tensor        # int32 [T, k]
+
+
+def q4_moe_route(logits: torch.Tensor, k: int, stream=None) -> Routing:
+    """Top-k routing with softmax gates and the expert-major dispatch order
+    for fp32 router logits [T, E] (unit column stride)."""
+    if logits.dtype != torch.float32 or logits.dim() != 2 or (logits.numel() and logits.stride(1) != 1):
+        raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
+    T, E = logits.shape
+    dev = logits.device
+    r = Routing(torch.empty((T, k), dtype=torch.int32, device=dev),
+                torch.empty((T, k), dtype=torch.float32, device=dev),
+                torch.empty(E + 1, dtype=torch.int32, device=dev),
+                torch.empty(T * k, dtype=torch.int32, device=dev),
+                torch.empty((T, k), dtype=torch.int32, device=dev))
+    _check(lib().q4_moe_route(_ptr(logits), logits.stride(0) if T else E, T, E, k, _ptr(r.ids), _ptr(r.weights),
+                              _ptr(r.offsets), _ptr(r.gather), _ptr(r.inv), _stream(stream)),
+           "q4_moe_route")
+    return r
+
+
+def q4_swiglu(gu: torch.Tensor, inter: int, h: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = silu(gu[:, :inter]) * gu[:, inter:2*inter] (bf16)."""
+    P = gu.shape[0]
+    if h is None:
+        h = torch.empty((P, inter), dtype=torch.bfloat16, device=gu.device)
+    _check(lib().q4_swiglu(_ptr(gu), gu.stride(0), P, inter, _ptr(h), h.stride(0), _stream(stream)),
+           "q4_swiglu")
+    return h
+
+
+def q4_moe_combine(y: torch.Tensor, r: Routing, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """out[t] = sum_j r.weights[t, j] * y[r.inv[t, j]] (bf16)."""
+    T, k = r.inv.shape
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
+    _check(lib().q4_moe_combine(_ptr(y), y.stride(0), _ptr(r.inv), _ptr(r.weights), T, k, N, _ptr(out),
+                                out.stride(0), _stream(stream)), "q4_moe_combine")
+    return out
+
+
+def moe_layer(x: torch.Tensor, logits: torch.Tensor, k: int, W_gu: Q4Tensor, W_down: Q4Tensor,
+              inter: int, stream=None):
+    """One MoE FFN layer: route, gate/up grouped GEMM, SwiGLU, down grouped
+    GEMM, combine -- five library calls on the same stream.  W_gu holds
+    [W_gate_e; W_up_e] (2*inter rows) per expert, W_down K rows per expert.
+    Returns (out [T, K] bf16, Routing)."""
+    T, K = x.shape
+    r = q4_moe_route(logits, k, stream)
+    P = T * k
+    gu = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=x.device)
+    q4_grouped_gemm(x, r.gather, r.offsets, W_gu, 2 * inter, gu, stream)
+    h = q4_swiglu(gu, inter, stream=stream)
+    y = torch.empty((P, K), dtype=torch.bfloat16, device=x.device)
+    q4_grouped_gemm(h, None, r.offsets, W_down, K, y, stream)
+    return q4_moe_combine(y, r, stream=stream), r

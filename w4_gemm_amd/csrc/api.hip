@@ -226,8 +226,9 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
   if (K % 128) return Q4_ERR_SHAPE;
   if (E == 0 || N == 0 || P == 0) return Q4_OK;
   if (K == 0) return Q4_ERR_SHAPE;
-  if (!gather || !expert_offsets) return Q4_ERR_NULL;
-  if (!aligned(gather, 4) || !aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
+  if (!expert_offsets) return Q4_ERR_NULL;
+  if (!gather && T < P) return Q4_ERR_SHAPE;  // identity gather reads rows 0..P-1 of A
+  if ((gather && !aligned(gather, 4)) || !aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
   st = check_bf16(A_bf16, T, K, lda);
   if (st != Q4_OK) return st;
   st = check_out_bf16(C_bf16, P, N, ldc);
@@ -237,6 +238,52 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
                                        static_cast<const uint8_t*>(W->codes), W->scales,
                                        W->global_scale, N, K, static_cast<uint16_t*>(C_bf16),
                                        ldc, as_stream(stream)));
+}
+
+q4_status q4_moe_route(const float* logits, int64_t ld, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                       float* topk_weights, int32_t* expert_offsets, int32_t* gather, int32_t* inv,
+                       void* stream) {
+  if (T < 0 || T >= kMaxDim || E < 1 || E > 1024 || k < 1 || k > 32 || k > E) return Q4_ERR_SHAPE;
+  if (q4::moe_dispatch_lds_bytes(T, E) > q4::kMoeDispatchMaxLds) return Q4_ERR_SHAPE;
+  if (!expert_offsets) return Q4_ERR_NULL;
+  if (!aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
+  if (T > 0) {
+    if (!logits || !topk_ids || !topk_weights || !gather || !inv) return Q4_ERR_NULL;
+    if (ld < E) return Q4_ERR_SHAPE;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4) || !aligned(gather, 4) ||
+        !aligned(inv, 4))
+      return Q4_ERR_ALIGN;
+  }
+  return hip_status(q4::launch_moe_route(logits, ld, T, E, k, topk_ids, topk_weights, expert_offsets, gather,
+                                         inv, as_stream(stream)));
+}
+
+q4_status q4_swiglu(const void* gu_bf16, int64_t ld_gu, int64_t P, int64_t I, void* h_bf16, int64_t ldh,
+                    void* stream) {
+  if (P < 0 || I < 0 || P >= kMaxDim || I >= kMaxDim) return Q4_ERR_SHAPE;
+  if (I % 8) return Q4_ERR_SHAPE;
+  if (P == 0 || I == 0) return Q4_OK;
+  q4_status st = check_bf16(gu_bf16, P, 2 * I, ld_gu);
+  if (st != Q4_OK) return st;
+  st = check_bf16(h_bf16, P, I, ldh);
+  if (st != Q4_OK) return st;
+  return hip_status(q4::launch_swiglu(static_cast<const uint16_t*>(gu_bf16), ld_gu, P, I,
+                                      static_cast<uint16_t*>(h_bf16), ldh, as_stream(stream)));
+}
+
+q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, const float* weights, int64_t T,
+                         int32_t k, int64_t N, void* out_bf16, int64_t ldo, void* stream) {
+  if (T < 0 || N < 0 || T >= kMaxDim || N >= kMaxDim || k < 1 || k > 32) return Q4_ERR_SHAPE;
+  if (N % 8) return Q4_ERR_SHAPE;
+  if (T == 0 || N == 0) return Q4_OK;
+  if (!inv || !weights) return Q4_ERR_NULL;
+  if (!aligned(inv, 4) || !aligned(weights, 4)) return Q4_ERR_ALIGN;
+  q4_status st = check_bf16(y_bf16, 1, N, ldy);
+  if (st != Q4_OK) return st;
+  st = check_bf16(out_bf16, T, N, ldo);
+  if (st != Q4_OK) return st;
+  return hip_status(q4::launch_moe_combine(static_cast<const uint16_t*>(y_bf16), ldy, inv, weights, T, k, N,
+                                           static_cast<uint16_t*>(out_bf16), ldo, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -1,6 +1,7 @@
 // grouped.hip -- grouped per-expert W4A16 GEMM (MoE) for expert weights in
 // the tiled layout: for every expert e and each routed row p in
-// [offsets[e], offsets[e+1]): C[p][n] = sum_k a[gather[p]][k] w'_e[n][k].
+// [offsets[e], offsets[e+1]): C[p][n] = sum_k a[gather[p]][k] w'_e[n][k]
+// (gather == NULL: row p of a).
 //
 // One low-bit weight matrix per expert with the tokens grouped by expert is
 // the MoE case of the W4A16 scheme ("Low-bit inference for very large MoE",
@@ -156,7 +157,7 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int p = c0 + xrow + 24 * j;
-      const int g = p < r1 ? gather[p] : -1;
+      const int g = p < r1 ? (gather ? gather[p] : p) : -1;
       srow[j] = (g >= 0 && g < T) ? g : 0;  // invalid rows staged from row 0, output zeroed
     }
     u32x4_t xr[2];
@@ -271,7 +272,7 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
         for (int bt = 0; bt < kBT; ++bt) {
           const int p = c0 + 16 * bt + (lane & 15);
           if (bt < nb && p < r1) {
-            const int g = gather[p];
+            const int g = gather ? gather[p] : p;
             const f32x4_t v = (g >= 0 && g < T) ? acc[t][bt] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             *reinterpret_cast<uint2*>(C + (int64_t)p * ldc + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
           }

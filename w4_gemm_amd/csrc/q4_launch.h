@@ -63,6 +63,24 @@ hipError_t launch_gemm_w4a8(int a_layout, int w_layout, const uint8_t* a_codes, 
                             int64_t M, const uint8_t* w_codes, const uint16_t* w_scales, int64_t N,
                             int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// MoE routing: top-k experts per token (ids, softmax gates) from fp32
+// logits [T][ld], then the expert-major dispatch (offsets [E+1], gather
+// [T*k], inv [T][k]) in one workgroup whose LDS holds per-expert token
+// bitmaps: moe_dispatch_lds_bytes(T, E) <= kMoeDispatchMaxLds.
+constexpr size_t kMoeDispatchMaxLds = 160 * 1024;
+size_t moe_dispatch_lds_bytes(int64_t T, int32_t E);
+hipError_t launch_moe_route(const float* logits, int64_t ld, int64_t T, int32_t E, int32_t k,
+                            int32_t* ids, float* weights, int32_t* offsets, int32_t* gather,
+                            int32_t* inv, hipStream_t stream);
+
+// h [P][ldh] = silu(gu[:, :I]) * gu[:, I:2I] (bf16), I % 8 == 0.
+hipError_t launch_swiglu(const uint16_t* gu, int64_t ld_gu, int64_t P, int64_t I, uint16_t* h, int64_t ldh,
+                         hipStream_t stream);
+
+// out [T][ldo] = sum_j w[t][j] * y[inv[t][j]] (bf16), N % 8 == 0.
+hipError_t launch_moe_combine(const uint16_t* y, int64_t ldy, const int32_t* inv, const float* w, int64_t T,
+                              int32_t k, int64_t N, uint16_t* out, int64_t ldo, hipStream_t stream);
+
 // Grouped expert GEMM with the expert weights in the tiled layout (K % 512
 // == 0, N % 16 == 0, T > 0): the weight-streaming kernel of grouped.hip.
 hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather,

@@ -67,6 +67,17 @@ def choose(name: str, population: int, count: int, seed: int = 0) -> np.ndarray:
     return np.sort(g.choice(population, size=count, replace=False))
 
 
+def normal_f32_range(name: str, lo: int, hi: int, seed: int = 0) -> np.ndarray:
+    """Values [lo, hi) of the named stream (the same numbers normal_f32
+    gives at those positions), generating only the chunks that cover them."""
+    c0, c1 = lo // CHUNK, (hi + CHUNK - 1) // CHUNK
+    out = np.empty((c1 - c0) * CHUNK, dtype=np.float32)
+    for i in range(c0, c1):
+        g = np.random.Generator(np.random.PCG64(_seedseq(seed, name, i)))
+        g.standard_normal(out=out[(i - c0) * CHUNK:(i - c0 + 1) * CHUNK], dtype=np.float32)
+    return out[lo - c0 * CHUNK:hi - c0 * CHUNK]
+
+
 def to_bf16(x: np.ndarray) -> torch.Tensor:
     """fp32 -> bf16 (round to nearest even), as a CPU tensor."""
     return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
@@ -92,13 +103,20 @@ def matrix(name: str, rows: int, cols: int, std: float, seed: int = 0,
     return to_bf16(x)
 
 
+def matrix_rows(name: str, rows: int, cols: int, std: float, r0: int, r1: int,
+                seed: int = 0) -> torch.Tensor:
+    """Rows [r0, r1) of matrix(name, rows, cols, std, seed) (no outliers)."""
+    assert 0 <= r0 <= r1 <= rows
+    x = normal_f32_range(name, r0 * cols, r1 * cols, seed) * np.float32(std)
+    return to_bf16(x.reshape(r1 - r0, cols))
+
+
 @dataclass
 class Routing:
     """Top-k routing of tokens to experts, rows grouped expert-major."""
     gather: np.ndarray        # int32 [P]: token of each routed row
     offsets: np.ndarray       # int32 [E+1]: rows of expert e are [offsets[e], offsets[e+1])
     topk_ids: np.ndarray      # int64 [T, k]
-    gates: np.ndarray         # fp32 [T, k]: softmax weight of each choice (combine step)
 
 
 def route(logits: np.ndarray, k: int) -> Routing:
@@ -107,10 +125,6 @@ def route(logits: np.ndarray, k: int) -> Routing:
     T, E = logits.shape
     order = np.argsort(-logits, axis=1, kind="stable")
     topk = order[:, :k]
-    z = logits - logits.max(axis=1, keepdims=True)
-    p = np.exp(z.astype(np.float64))
-    p /= p.sum(axis=1, keepdims=True)
-    gates = np.take_along_axis(p, topk, axis=1).astype(np.float32)
     counts = np.bincount(topk.ravel(), minlength=E)
     offsets = np.zeros(E + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
@@ -120,7 +134,7 @@ def route(logits: np.ndarray, k: int) -> Routing:
         for e in topk[t]:
             gather[fill[e]] = t
             fill[e] += 1
-    return Routing(gather, offsets.astype(np.int32), topk, gates)
+    return Routing(gather, offsets.astype(np.int32), topk)
 
 
 # --------------------------------------------------------------------------
@@ -176,6 +190,30 @@ def w4a8_gemm(seed: int = 0, m: int = 4096, n: int = 8192, k: int = 8192) -> Wor
     a = matrix("w4a8/A", m, k, 1.0, seed, channel_frac=0.01, channel_mult=10.0)
     w = matrix("w4a8/W", n, k, 0.02, seed)
     return Workload("w4a8_int4_fp8_gemm", "int4", {"A": a, "W": w}, {"M": m, "N": n, "K": k})
+
+
+def moe_layer(seed: int = 0, experts: int = 64, inter: int = 2048, hidden: int = 7168,
+              tokens: int = 256, topk: int = 8) -> Workload:
+    """MoE FFN layer around the grouped GEMM, the MoE workload's shapes:
+    x [tokens, hidden] and router logits [tokens, experts] are the MoE
+    workload's A and logits; per expert e, W_up_e is rows [e*inter, (e+1)*
+    inter) of its W, W_gate_e the same rows of the stream "moe/Wgate" and
+    W_down_e rows [e*hidden, (e+1)*hidden) of "moe/Wdown" [experts*hidden,
+    inter], all ~ N(0, 0.02^2).  `expert(e)` returns (W_gu_e = [W_gate_e;
+    W_up_e] bf16 [2*inter, hidden], W_down_e bf16 [hidden, inter]) without
+    generating the other experts."""
+    a = matrix("moe/A", tokens, hidden, 1.0, seed)
+    logits = normal_f32("moe/logits", tokens * experts, seed).reshape(tokens, experts)
+
+    def expert(e):
+        up = matrix_rows("moe/W", experts * inter, hidden, 0.02, e * inter, (e + 1) * inter, seed)
+        gate = matrix_rows("moe/Wgate", experts * inter, hidden, 0.02, e * inter, (e + 1) * inter, seed)
+        down = matrix_rows("moe/Wdown", experts * hidden, inter, 0.02, e * hidden, (e + 1) * hidden, seed)
+        return torch.cat([gate, up]), down
+
+    return Workload("moe_layer_mxfp4", "mxfp4", {"x": a},
+                    {"E": experts, "I": inter, "K": hidden, "T": tokens, "topk": topk,
+                     "logits": logits, "expert": expert})
 
 
 def w4a4_gemm(seed: int = 0, m: int = 8192, n: int = 8192, k: int = 8192) -> Workload:
