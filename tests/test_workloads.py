@@ -43,4 +43,3 @@ def test_route_top_k_and_counting_sort():
         toks = r.gather[r.offsets[e]:r.offsets[e + 1]]
         assert np.all(np.diff(toks) > 0)              # tokens ascending within an expert
         assert all(e in r.topk_ids[t] for t in toks)
-    assert np.allclose(r.gates.sum(1) <= 1.0 + 1e-6, True)
