@@ -374,25 +374,33 @@ def bench_moe_layer(torch, q4, workloads, dev, seed):
     y = torch.empty((P, K), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
     L = q4.lib()
+    # the gate/up weight read as [W_gate_e; W_up_e] (unfused path) or in the
+    # alternating-tile order of the fused gate/up + SwiGLU kernel: random
+    # rows either way, so the two paths stream the same bytes
     steps = {
         "route": lambda: q4.q4_moe_route(logits, k),
+        "gate_up_swiglu_fused": lambda: q4.q4_grouped_gemm_swiglu(x, r.gather, r.offsets, qgu, I, h),
         "gate_up": lambda: q4.q4_grouped_gemm(x, r.gather, r.offsets, qgu, 2 * I, gu),
         "swiglu": lambda: q4.q4_swiglu(gu, I, h),
         "down": lambda: q4.q4_grouped_gemm(h, None, r.offsets, qd, K, y),
         "combine": lambda: q4.q4_moe_combine(y, r, out),
     }
 
-    def layer():
+    def route():
         q4._check(L.q4_moe_route(q4._ptr(logits), E, T, E, k, q4._ptr(r.ids), q4._ptr(r.weights),
                                  q4._ptr(r.offsets), q4._ptr(r.gather), q4._ptr(r.inv), q4._stream(None)),
                   "q4_moe_route")
-        for name in ("gate_up", "swiglu", "down", "combine"):
+
+    def layer(fused):
+        route()
+        for name in (("gate_up_swiglu_fused",) if fused else ("gate_up", "swiglu")) + ("down", "combine"):
             steps[name]()
 
-    ms = timed(torch, layer, 10, 2)
+    ms = timed(torch, lambda: layer(True), 10, 2)
+    ms_unfused = timed(torch, lambda: layer(False), 10, 2)
     per = {n: round(timed(torch, f, 10, 2) * 1e3, 1) for n, f in steps.items()}
     wbytes = qgu.nbytes + qd.nbytes
-    return {"us": round(ms * 1e3, 1), "weight_bytes": wbytes,
+    return {"us": round(ms * 1e3, 1), "us_unfused": round(ms_unfused * 1e3, 1), "weight_bytes": wbytes,
             "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "steps_us": per, "tokens": T, "topk": k}

@@ -228,6 +228,22 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
  */
 
 /*
+ * The gate/up expert GEMM with the SwiGLU activation fused into its
+ * epilogue: for expert e and routed row p,
+ *     H[p][n] = bf16(silu(sum_k a[k] w_gate_e[n][k]) * sum_k a[k] w_up_e[n][k])
+ * with a = A[gather[p]] as in q4_grouped_gemm (NULL gather = identity).
+ * W (tiled layout only, else Q4_ERR_FORMAT) holds 2I rows per expert that
+ * alternate 16-row tiles of W_gate and W_up: rows e*2I + 32j + r are gate
+ * row 16j + r and rows e*2I + 32j + 16 + r are up row 16j + r (r < 16);
+ * I % 16 == 0.  H_bf16 [P][ldh].  Replaces q4_grouped_gemm + q4_swiglu
+ * without writing the gate/up products.
+ */
+q4_status q4_grouped_gemm_swiglu(const void* A_bf16, int64_t lda, int64_t T, const int32_t* gather,
+                                 const int32_t* expert_offsets, int32_t E, int64_t P,
+                                 const q4_tensor* W, int64_t I, void* H_bf16, int64_t ldh,
+                                 void* stream);
+
+/*
  * Routing of T tokens over E experts from fp32 router logits [T][ld].
  * Token t's experts are its k largest logits, largest first, ties to the
  * lower expert id: topk_ids [T][k]; its gate for each is that expert's

@@ -141,3 +141,63 @@ def test_moe_layer_expert_shape():
                                oracle.quantize("mxfp4", to_f32(wd)), I, tokens=tokens)
     assert np.array_equal(r.ids.cpu().numpy(), rr.ids)
     _check_layer(out[tokens], ref, "moe layer 2048x7168")
+
+
+@pytest.mark.parametrize("fmt", ("mxfp4", "int4", "nvfp4"))
+@pytest.mark.parametrize("E,I,K,T,k", [(8, 512, 1024, 37, 2), (4, 272, 512, 300, 2)])
+def test_grouped_gemm_swiglu(fmt, E, I, K, T, k):
+    """The fused gate/up + SwiGLU epilogue against the oracle's grouped GEMM
+    followed by SwiGLU; bad gather rows give zero rows."""
+    log("grouped gemm swiglu", fmt, E, I, K, T, k)
+    wgu = workloads.matrix(f"tmoe/fw{E}x{I}x{K}", E * 2 * I, K, 0.03, seed=90)
+    a = workloads.matrix(f"tmoe/fa{T}x{K}", T, K, 1.0, seed=91)
+    lg = _logits(T, E, seed=92)
+    rr = oracle.moe_route(lg, k)
+    gather = rr.gather.copy()
+    gather[5] = -1
+    gather[7] = T + 3
+    qw = q4.quantize(q4.interleave_gate_up(wgu, E, I).to(DEV), fmt, layout="tiled")
+    P = len(gather)
+    H = torch.full((P, I + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q4.q4_grouped_gemm_swiglu(a.to(DEV), torch.from_numpy(gather).to(DEV), torch.from_numpy(rr.offsets).to(DEV),
+                              qw, I, H[:, :I])
+    torch.cuda.synchronize()
+    Hc = H.cpu()
+    assert torch.isnan(Hc[:, I:]).all()
+    got = to_f32(Hc[:, :I]).astype(np.float64)
+    qr = oracle.quantize(fmt, to_f32(wgu))
+    gu = oracle.grouped_gemm(to_f32(a), np.clip(gather, 0, T - 1), rr.offsets, qr, 2 * I)
+    ref = oracle.swiglu(gu, I)
+    bad_rows = [5, 7]
+    ref[bad_rows] = 0.0
+    assert np.all(got[bad_rows] == 0.0)
+    # error bound: bf16 output rounding plus the propagated error of the two sums
+    af = np.abs(to_f32(a).astype(np.float64))
+    wd = np.abs(oracle.dequant(qr).astype(np.float64))
+    S = np.zeros((P, 2 * I))
+    for e in range(E):
+        lo, hi = rr.offsets[e], rr.offsets[e + 1]
+        S[lo:hi] = af[np.clip(gather[lo:hi], 0, T - 1)] @ wd[e * 2 * I:(e + 1) * 2 * I].T
+    c = 2.0 ** -16 if fmt == "mxfp4" else 2.0 ** -8
+    g, u = gu[:, :I], gu[:, I:]
+    bound = 2.0 ** -8 * np.abs(ref) + 1.1 * c * (S[:, :I] * np.abs(u) + np.abs(g) * S[:, I:]) + c * c * S[:, :I] * S[:, I:] + 1e-30
+    bound[bad_rows] = 0.0
+    bad = np.argwhere(np.abs(got - ref) > bound)
+    assert bad.size == 0, [(int(i), int(j), got[i, j], ref[i, j]) for i, j in bad[:5]]
+
+
+@pytest.mark.parametrize("fmt", ("mxfp4", "nvfp4"))
+def test_moe_layer_fused(fmt):
+    E, I, K, T, k = 8, 512, 1024, 37, 2
+    log("moe layer fused", fmt)
+    wgu = workloads.matrix("tmoe/wgu", E * 2 * I, K, 0.03, seed=86)
+    wd = workloads.matrix("tmoe/wd", E * K, I, 0.03, seed=87)
+    x = workloads.matrix("tmoe/x", T, K, 1.0, seed=88)
+    lg = _logits(T, E, seed=89)
+    qgu = q4.quantize(q4.interleave_gate_up(wgu, E, I).to(DEV), fmt, layout="tiled")
+    qd = q4.quantize(wd.to(DEV), fmt, layout="tiled")
+    out, r = q4.moe_layer(x.to(DEV), torch.from_numpy(lg).to(DEV), k, qgu, qd, I, fused=True)
+    torch.cuda.synchronize()
+    ref, rr = oracle.moe_layer(to_f32(x), lg, k, oracle.quantize(fmt, to_f32(wgu)),
+                               oracle.quantize(fmt, to_f32(wd)), I)
+    _check_layer(out, ref, f"moe layer fused {fmt}")

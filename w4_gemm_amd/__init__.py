@@ -21,7 +21,8 @@ __all__ = [
     "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
-    "q4_grouped_gemm", "q4_moe_route", "q4_swiglu", "q4_moe_combine", "moe_layer",
+    "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
+    "moe_layer", "interleave_gate_up",
     "empty_q4", "quantize", "LIB_PATH",
 ]
 
@@ -81,6 +82,8 @@ def _lib_handle():
             "q4_gemm": ([i64, vp, i64, P, P, vp, i64, vp], ctypes.c_int),
             "q4_grouped_gemm": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
                                 ctypes.c_int),
+            "q4_grouped_gemm_swiglu": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
+                                       ctypes.c_int),
             "q4_moe_route": ([vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "q4_swiglu": ([vp, i64, i64, i64, vp, i64, vp], ctypes.c_int),
             "q4_moe_combine": ([vp, i64, vp, vp, i64, i32, i64, vp, i64, vp], ctypes.c_int),
@@ -318,18 +321,48 @@ def q4_moe_combine(y: torch.Tensor, r: Routing, out: Optional[torch.Tensor] = No
     return out
 
 
+def q4_grouped_gemm_swiglu(A: torch.Tensor, gather: Optional[torch.Tensor], offsets: torch.Tensor,
+                           W: Q4Tensor, inter: int, H: torch.Tensor, stream=None) -> torch.Tensor:
+    """H[p] = silu(A[gather[p]] . W_gate_e^T) * (A[gather[p]] . W_up_e^T),
+    with W's 2*inter rows per expert alternating 16-row gate and up tiles
+    (see interleave_gate_up); gather None: row p reads A[p]."""
+    if (gather is not None and gather.dtype != torch.int32) or offsets.dtype != torch.int32:
+        raise ValueError("gather and offsets must be int32")
+    E = offsets.numel() - 1
+    P = H.shape[0] if gather is None else gather.numel()
+    wd = W.c()
+    _check(lib().q4_grouped_gemm_swiglu(_ptr(A), A.stride(0), A.shape[0], _ptr(gather), _ptr(offsets), E, P,
+                                        ctypes.byref(wd), inter, _ptr(H), H.stride(0), _stream(stream)),
+           "q4_grouped_gemm_swiglu")
+    return H
+
+
+def interleave_gate_up(w_gu: torch.Tensor, experts: int, inter: int) -> torch.Tensor:
+    """[W_gate_e; W_up_e] per expert (2*inter rows each) -> the row order
+    q4_grouped_gemm_swiglu takes: 16-row tiles alternating gate and up
+    (a permutation of rows, done before quantization)."""
+    K = w_gu.shape[1]
+    w = w_gu.reshape(experts, 2, inter // 16, 16, K)       # expert, gate/up, tile, row, k
+    return w.permute(0, 2, 1, 3, 4).reshape(experts * 2 * inter, K).contiguous()
+
+
 def moe_layer(x: torch.Tensor, logits: torch.Tensor, k: int, W_gu: Q4Tensor, W_down: Q4Tensor,
-              inter: int, stream=None):
+              inter: int, stream=None, fused: bool = False):
     """One MoE FFN layer: route, gate/up grouped GEMM, SwiGLU, down grouped
-    GEMM, combine -- five library calls on the same stream.  W_gu holds
-    [W_gate_e; W_up_e] (2*inter rows) per expert, W_down K rows per expert.
-    Returns (out [T, K] bf16, Routing)."""
+    GEMM, combine -- library calls on the same stream.  W_gu holds
+    [W_gate_e; W_up_e] (2*inter rows) per expert, or with fused=True the
+    interleave_gate_up order (then q4_grouped_gemm_swiglu makes h directly);
+    W_down has K rows per expert.  Returns (out [T, K] bf16, Routing)."""
     T, K = x.shape
     r = q4_moe_route(logits, k, stream)
     P = T * k
-    gu = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=x.device)
-    q4_grouped_gemm(x, r.gather, r.offsets, W_gu, 2 * inter, gu, stream)
-    h = q4_swiglu(gu, inter, stream=stream)
+    if fused:
+        h = torch.empty((P, inter), dtype=torch.bfloat16, device=x.device)
+        q4_grouped_gemm_swiglu(x, r.gather, r.offsets, W_gu, inter, h, stream)
+    else:
+        gu = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=x.device)
+        q4_grouped_gemm(x, r.gather, r.offsets, W_gu, 2 * inter, gu, stream)
+        h = q4_swiglu(gu, inter, stream=stream)
     y = torch.empty((P, K), dtype=torch.bfloat16, device=x.device)
     q4_grouped_gemm(h, None, r.offsets, W_down, K, y, stream)
     return q4_moe_combine(y, r, stream=stream), r

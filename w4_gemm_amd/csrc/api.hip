@@ -240,6 +240,30 @@ q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int3
                                        ldc, as_stream(stream)));
 }
 
+q4_status q4_grouped_gemm_swiglu(const void* A_bf16, int64_t lda, int64_t T, const int32_t* gather,
+                                 const int32_t* expert_offsets, int32_t E, int64_t P, const q4_tensor* W,
+                                 int64_t I, void* H_bf16, int64_t ldh, void* stream) {
+  q4_status st = check_tensor(W);
+  if (st != Q4_OK) return st;
+  if (W->fmt == Q4_FP8_ROW || W->layout != Q4_LAYOUT_TILED) return Q4_ERR_FORMAT;
+  if (E < 0 || E > 65535 || I < 0 || T < 0 || P < 0 || P >= kMaxDim || T >= kMaxDim) return Q4_ERR_SHAPE;
+  if (I % 16 || W->rows != (int64_t)E * 2 * I) return Q4_ERR_SHAPE;
+  const int64_t K = W->cols;
+  if (E == 0 || I == 0 || P == 0) return Q4_OK;
+  if (K == 0 || T == 0) return Q4_ERR_SHAPE;
+  if (!expert_offsets) return Q4_ERR_NULL;
+  if (!gather && T < P) return Q4_ERR_SHAPE;
+  if ((gather && !aligned(gather, 4)) || !aligned(expert_offsets, 4)) return Q4_ERR_ALIGN;
+  st = check_bf16(A_bf16, T, K, lda);
+  if (st != Q4_OK) return st;
+  st = check_bf16(H_bf16, P, I, ldh);
+  if (st != Q4_OK) return st;
+  return hip_status(q4::launch_grouped_tiled_swiglu(
+      W->fmt, static_cast<const uint16_t*>(A_bf16), lda, T, gather, expert_offsets, E, P,
+      static_cast<const uint8_t*>(W->codes), W->scales, W->global_scale, 2 * I, K, static_cast<uint16_t*>(H_bf16),
+      ldh, as_stream(stream)));
+}
+
 q4_status q4_moe_route(const float* logits, int64_t ld, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
                        float* topk_weights, int32_t* expert_offsets, int32_t* gather, int32_t* inv,
                        void* stream) {

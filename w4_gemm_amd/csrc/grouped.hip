@@ -91,7 +91,11 @@ struct ScaleW {
   uint32_t w[NSW];
 };
 
-template <int FMT>
+// SWIGLU: the expert's weight rows alternate 16-row tiles of W_gate and
+// W_up (tile 2j = gate rows 16j.., tile 2j+1 = up rows 16j..), so a wave's
+// two tiles are the gate and up rows of the same 16 outputs and the
+// epilogue writes h = silu(gate) * up (N/2 columns) instead of both.
+template <int FMT, bool SWIGLU>
 __global__ void __launch_bounds__(kWaves * 64)
 grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
                      const int32_t* __restrict__ gather, const int32_t* __restrict__ offsets, int P,
@@ -264,6 +268,28 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
 
     // tile t, batch tile bt: lane l, register q holds C[p][n] with
     // p = c0 + 16bt + l%16 and n = 16(tile0+t) + 4(l/16) + q
+    if constexpr (SWIGLU) {
+      static_assert(kTPW == 2, "a wave holds one gate tile and its up tile");
+      if (tile0 + 1 < NT) {
+        const int n = 8 * tile0 + 4 * (lane >> 4);  // output column: 16 * (gate tile index) + ...
+#pragma unroll
+        for (int bt = 0; bt < kBT; ++bt) {
+          const int p = c0 + 16 * bt + (lane & 15);
+          if (bt < nb && p < r1) {
+            const int g = gather ? gather[p] : p;
+            f32x4_t v = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            if (g >= 0 && g < T) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float z = acc[0][bt][q];
+                v[q] = z / (1.0f + expf(-z)) * acc[1][bt][q];
+              }
+            }
+            *reinterpret_cast<uint2*>(C + (int64_t)p * ldc + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int t = 0; t < kTPW; ++t) {
       if (tile0 + t < NT) {
@@ -279,21 +305,22 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
         }
       }
     }
+    }
     stage_barrier();  // the next chunk reuses the LDS buffers
   }
 }
 
-template <int FMT>
+template <int FMT, bool SWIGLU>
 hipError_t run(const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather, const int32_t* offsets,
                int32_t E, int64_t P, const uint8_t* codes, const void* scales, const float* gs,
                int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&grouped_tiled_kernel<FMT>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&grouped_tiled_kernel<FMT, SWIGLU>), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)kSmemBytes);
   if (attr != hipSuccess) return attr;
   const int64_t NT = N / 16;
   const dim3 grid((unsigned)((NT + kWaves * kTPW - 1) / (kWaves * kTPW)), (unsigned)E);
-  grouped_tiled_kernel<FMT><<<grid, kWaves * 64, kSmemBytes, stream>>>(
+  grouped_tiled_kernel<FMT, SWIGLU><<<grid, kWaves * 64, kSmemBytes, stream>>>(
       A, lda, (int)T, gather, offsets, (int)P, codes, static_cast<const uint8_t*>(scales), gs, (int)N,
       (int)K, C, ldc);
   return hipGetLastError();
@@ -306,9 +333,19 @@ hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t
                                 const void* scales, const float* gs, int64_t N, int64_t K, uint16_t* C,
                                 int64_t ldc, hipStream_t stream) {
   if (E == 0 || N == 0 || P == 0) return hipSuccess;
-  if (fmt == 0) return run<0>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
-  if (fmt == 1) return run<1>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
-  return run<2>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 0) return run<0, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 1) return run<1, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
+  return run<2, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
+}
+
+hipError_t launch_grouped_tiled_swiglu(int fmt, const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather,
+                                       const int32_t* offsets, int32_t E, int64_t P, const uint8_t* codes,
+                                       const void* scales, const float* gs, int64_t N2, int64_t K, uint16_t* H,
+                                       int64_t ldh, hipStream_t stream) {
+  if (E == 0 || N2 == 0 || P == 0) return hipSuccess;
+  if (fmt == 0) return run<0, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
+  if (fmt == 1) return run<1, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
+  return run<2, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
 }
 
 }  // namespace q4

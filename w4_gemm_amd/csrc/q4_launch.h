@@ -88,6 +88,13 @@ hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t
                                 const void* scales, const float* gs, int64_t N, int64_t K, uint16_t* C,
                                 int64_t ldc, hipStream_t stream);
 
+// The same kernel with the SwiGLU epilogue: each expert's 2I weight rows
+// alternate 16-row tiles of W_gate and W_up; writes H [P][ldh] (I columns).
+hipError_t launch_grouped_tiled_swiglu(int fmt, const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather,
+                                       const int32_t* offsets, int32_t E, int64_t P, const uint8_t* codes,
+                                       const void* scales, const float* gs, int64_t N2, int64_t K, uint16_t* H,
+                                       int64_t ldh, hipStream_t stream);
+
 // Grouped expert GEMM (W4A16), see q4_grouped_gemm.
 hipError_t launch_grouped(int fmt, int layout, const uint16_t* A, int64_t lda, int64_t T,
                           const int32_t* gather, const int32_t* offsets, int32_t E, int64_t P,
