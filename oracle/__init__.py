@@ -39,8 +39,8 @@ from . import build as _build
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-FORMATS = ("int4", "mxfp4", "nvfp4")
-GROUP = {"int4": 128, "mxfp4": 32, "nvfp4": 16}
+FORMATS = ("int4", "mxfp4", "nvfp4", "int4_zp")
+GROUP = {"int4": 128, "mxfp4": 32, "nvfp4": 16, "int4_zp": 128}
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -92,6 +92,12 @@ def lib():
         L.oracle_quantize_fp8_rows.restype = None
         L.oracle_dequant_fp8_rows.argtypes = [_p, _p, _i64, _i64, _p]
         L.oracle_dequant_fp8_rows.restype = None
+        L.oracle_int4zp_group.argtypes = [_p, _i64, _p]
+        L.oracle_int4zp_group.restype = ctypes.c_uint32
+        L.oracle_quantize_int4zp.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+        L.oracle_quantize_int4zp.restype = ctypes.c_int
+        L.oracle_dequant_int4zp.argtypes = [_p, _p, _i64, _i64, _p]
+        L.oracle_dequant_int4zp.restype = None
         L.oracle_dequant_int4.argtypes = [_p, _p, _i64, _i64, _i64, _p]
         L.oracle_dequant_int4.restype = None
         L.oracle_dequant_mxfp4.argtypes = [_p, _p, _i64, _i64, _p]
@@ -203,6 +209,10 @@ def quantize(fmt: str, w, gs: float | None = None) -> QTensor:
         scales = np.zeros((rows, cols // g), dtype=np.uint8)
         rc = L.oracle_quantize_mxfp4(_ptr(w), rows, cols, cols, _ptr(codes), _ptr(scales))
         out_gs = None
+    elif fmt == "int4_zp":
+        scales = np.zeros((rows, cols // g), dtype=np.uint32)
+        rc = L.oracle_quantize_int4zp(_ptr(w), rows, cols, cols, _ptr(codes), _ptr(scales))
+        out_gs = None
     elif fmt == "nvfp4":
         scales = np.zeros((rows, cols // g), dtype=np.uint8)
         gs_out = np.zeros(1, dtype=np.float32)
@@ -216,6 +226,14 @@ def quantize(fmt: str, w, gs: float | None = None) -> QTensor:
     if rc != 0:
         raise ValueError(f"oracle quantize failed ({rc})")
     return QTensor(fmt, rows, cols, codes, scales, out_gs)
+
+
+def int4zp_group(w):
+    """(scale word, codes) of one group of INT4 with a zero point."""
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.float32))
+    q = np.zeros(len(w), dtype=np.int32)
+    word = int(lib().oracle_int4zp_group(_ptr(w), len(w), _ptr(q)))
+    return word, q
 
 
 def nv_global_scale(w) -> float:
@@ -233,6 +251,8 @@ def dequant(q: QTensor) -> np.ndarray:
         L.oracle_dequant_int4(_ptr(codes), _ptr(scales), q.rows, q.cols, 128, _ptr(out))
     elif q.fmt == "mxfp4":
         L.oracle_dequant_mxfp4(_ptr(codes), _ptr(scales), q.rows, q.cols, _ptr(out))
+    elif q.fmt == "int4_zp":
+        L.oracle_dequant_int4zp(_ptr(codes), _ptr(scales), q.rows, q.cols, _ptr(out))
     else:
         L.oracle_dequant_nvfp4(_ptr(codes), _ptr(scales), q.gs, q.rows, q.cols, _ptr(out))
     return out

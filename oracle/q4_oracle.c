@@ -265,6 +265,93 @@ void oracle_dequant_int4(const uint8_t* codes, const uint16_t* scales, int64_t r
 }
 
 /* ------------------------------------------------------------------------ */
+/* INT4 with a zero point: integers -8..7, one fp16 scale and one zero point */
+/* per group of 128 ("Quantization in deployment", format cheat sheet, row    */
+/* W4A16 INT4 GPTQ/AWQ: one scale per 128 numbers, plus a zero point; the   */
+/* zero point absorbs a constant offset of the group).  Readings (min-max   */
+/* rounding, the rule of the GPTQ/AWQ formats that row names):              */
+/*   lo = min(min_group, 0), hi = max(max_group, 0)   (0 stays exact)        */
+/*   scale = fp16(fp32(hi - lo) / 15)                                        */
+/*   z = clamp(-8 - rne(lo / scale), -8, 7)            (an integer code)     */
+/*   q = clamp(rne(w / scale) + z, -8, 7),  value = (q - z) * scale          */
+/* A group whose fp16 scale is 0 stores scale 0, zero point 0 and codes 0.   */
+/* Storage: codes as INT4 (two's complement nibbles); one 32-bit word per    */
+/* group = fp16 scale bits | (z & 0xFF) << 16.                               */
+/* ------------------------------------------------------------------------ */
+
+uint32_t oracle_int4zp_group(const float* w, int64_t n, int32_t* q_out)
+{
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        if (w[i] < lo)
+            lo = w[i];
+        if (w[i] > hi)
+            hi = w[i];
+    }
+    float range = hi - lo;                     /* fp32 */
+    int s_code = oracle_fp16_code(range / 15.0f);
+    float s = oracle_fp16_value(s_code);
+    if (s == 0.0f) {
+        for (int64_t i = 0; i < n; ++i)
+            q_out[i] = 0;
+        return 0u;
+    }
+    float zr = -8.0f - rintf(lo / s);          /* divide by the stored scale */
+    if (zr < -8.0f)
+        zr = -8.0f;
+    if (zr > 7.0f)
+        zr = 7.0f;
+    int z = (int)zr;
+    for (int64_t i = 0; i < n; ++i) {
+        float qr = rintf(w[i] / s) + (float)z;
+        if (qr > 7.0f)
+            qr = 7.0f;
+        if (qr < -8.0f)
+            qr = -8.0f;
+        q_out[i] = (int32_t)qr;
+    }
+    return (uint32_t)s_code | ((uint32_t)(z & 0xFF) << 16);
+}
+
+int oracle_quantize_int4zp(const float* w, int64_t rows, int64_t cols, int64_t ld, uint8_t* codes,
+                           uint32_t* scales)
+{
+    const int64_t g = 128;
+    if (cols % g != 0)
+        return -1;
+    int64_t nb = cols / g;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int32_t q[128];
+        uint8_t* rc = codes + r * (cols / 2);
+        for (int64_t b = 0; b < nb; ++b) {
+            scales[r * nb + b] = oracle_int4zp_group(w + r * ld + b * g, g, q);
+            for (int64_t i = 0; i < g; ++i)
+                put_nibble(rc, b * g + i, q[i] & 0xF);
+        }
+    }
+    return 0;
+}
+
+/* value = fp32((q - z) * scale), exact (|q - z| <= 15, an fp16 scale). */
+void oracle_dequant_int4zp(const uint8_t* codes, const uint32_t* scales, int64_t rows, int64_t cols,
+                           float* out)
+{
+    int64_t nb = cols / 128;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t k = 0; k < cols; ++k) {
+            int nib = get_nibble(codes + r * (cols / 2), k);
+            int q = (nib >= 8) ? nib - 16 : nib;
+            uint32_t word = scales[r * nb + k / 128];
+            float s = oracle_fp16_value((int)(word & 0xFFFFu));
+            int z = (int)(int8_t)((word >> 16) & 0xFFu);
+            out[r * cols + k] = (float)(q - z) * s;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* E2M1 element encode shared by MXFP4 and NVFP4: y = clamp(w/scale, -6, 6),  */
 /* nearest grid value; sign bit from w.                                       */
 /* ------------------------------------------------------------------------ */
