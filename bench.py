@@ -239,6 +239,21 @@ def main():
         extra["decode_gemv_rowmajor_us"][str(b)] = round(gt.per_launch_ms(5) * 1e3, 3)
     del rows_copies
 
+    # the same decode GEMV on the other tiled weight formats of the same
+    # shape (INT4 g128, NVFP4, INT4 with a zero point), rotating copies
+    extra["decode_gemv_tiled_other_formats_us"] = {}
+    for fmt in ("int4", "nvfp4", "int4_zp"):
+        fc = [q4.quantize(W, fmt, layout="tiled")]
+        fc += [fc[0].clone() for _ in range(args.copies - 1)]
+        fb = fc[0].nbytes
+        res = {"weight_bytes": fb}
+        for b in batches:
+            gt = GraphTimer(torch, lambda i, b=b: q4.q4_gemv(fc[i % ncopy], xs[b], ys[b]), per_graph=ncopy * 4)
+            us = gt.per_launch_ms(5) * 1e3
+            res[str(b)] = {"us": round(us, 3), "weight_GBps": round(fb / (us * 1e-6) / 1e9, 1)}
+        extra["decode_gemv_tiled_other_formats_us"][fmt] = res
+        del fc
+
     # quantization of the decode weight
     empty = q4.empty_q4("mxfp4", N, K, device=dev, layout="tiled")
     ms = timed(torch, lambda: q4.q4_quantize(W, empty), 10, 3)

@@ -18,6 +18,16 @@
  *                 block scale = E4M3(min(amax_b/6/gs, 448)), element
  *                 divided by E4M3(scale)*gs.  ("Quantization in deployment",
  *                 formats.py nvfp4(); "Quantization chains", NVFP4 vs MXFP4.)
+ *   Q4_INT4_ZP_G128  INT4 with a zero point: codes -8..7 (4-bit two's
+ *                 complement), per group of 128 one fp16 scale and one zero
+ *                 point z (an integer code), value = (q - z) * scale; min-max
+ *                 rounding over the group widened to include 0: lo =
+ *                 min(min,0), hi = max(max,0), scale = fp16((hi-lo)/15),
+ *                 z = clamp(-8 - rne(lo/scale), -8, 7), q = clamp(rne(w/
+ *                 scale) + z, -8, 7).  ("Quantization in deployment",
+ *                 format cheat sheet, W4A16 INT4 GPTQ/AWQ row: one scale
+ *                 per 128 numbers plus a zero point.)  Scales are 32-bit
+ *                 words: fp16 bits | (z & 0xFF) << 16.
  *   Q4_FP8_ROW    the activation operand of W4A8, not a weight format:
  *                 one E4M3 byte per value and one fp32 scale per row
  *                 (token), scale = max(amax_row,1e-12)/448, code =
@@ -36,7 +46,8 @@
  * Q4_LAYOUT_ROWS (row-major, dense):
  *   codes   uint8 [rows][cols/2], 16-byte aligned.
  *   scales  INT4: fp16 bits [rows][cols/128]; MXFP4: biased E8M0 exponent
- *           [rows][cols/32]; NVFP4: E4M3 bits [rows][cols/16].  4-byte aligned.
+ *           [rows][cols/32]; NVFP4: E4M3 bits [rows][cols/16]; INT4 with a
+ *           zero point: 32-bit words [rows][cols/128].  4-byte aligned.
  *
  * Q4_LAYOUT_TILED (the weights pre-shuffled so that one 64-lane load is one
  * contiguous kilobyte holding a whole matrix-core operand; cols % 512 == 0).
@@ -52,7 +63,9 @@
  *           NVFP4: byte ((t*Q + q)*64 + l)*8 + 2i + h is the E4M3 of row
  *                  16t+n, 16-block 8(4q+i) + 2g + h    (RT*Q*512 bytes);
  *           INT4:  fp16 element ((t*Q + q)*16 + n)*4 + i is the scale of
- *                  row 16t+n, 128-group 4q + i          (RT*Q*128 bytes).
+ *                  row 16t+n, 128-group 4q + i          (RT*Q*128 bytes);
+ *           INT4 with a zero point: the 32-bit word at the same element
+ *                  index                                (RT*Q*256 bytes).
  *   Padding rows (16t+n >= rows) hold the quantization of zeros.
  *
  * Q4_FP8_ROW in the two layouts (cols % 16 == 0 row-major, % 512 tiled):
@@ -95,7 +108,8 @@ typedef enum q4_format {
     Q4_INT4_G128 = 0,
     Q4_MXFP4 = 1,
     Q4_NVFP4 = 2,
-    Q4_FP8_ROW = 3
+    Q4_FP8_ROW = 3,
+    Q4_INT4_ZP_G128 = 4
 } q4_format;
 
 typedef enum q4_layout {

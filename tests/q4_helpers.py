@@ -17,7 +17,7 @@ import torch
 
 import oracle
 
-FMT_ID = {"int4": 0, "mxfp4": 1, "nvfp4": 2}
+FMT_ID = {"int4": 0, "mxfp4": 1, "nvfp4": 2, "int4_zp": 4}
 
 
 def log(*a):
@@ -33,6 +33,8 @@ def scales_np(q, fmt):
     s = q.scales.cpu()
     if fmt == "int4":
         return s.view(torch.int16).numpy().view(np.uint16)
+    if fmt == "int4_zp":
+        return s.view(torch.int32).numpy().view(np.uint32)
     return s.numpy()
 
 

@@ -49,6 +49,7 @@ def test_status_strings():
 
 @pytest.mark.parametrize("fmt,cols,codes,scales", [
     (q4.INT4_G128, 1024, 512, 16), (q4.MXFP4, 1024, 512, 32), (q4.NVFP4, 1024, 512, 64),
+    (q4.INT4_ZP, 1024, 512, 32),
 ])
 def test_sizes(fmt, cols, codes, scales):
     assert q4.q4_sizes(fmt, 1, cols) == (codes, scales)

@@ -14,8 +14,8 @@ from q4_helpers import check_matmul, log, to_f32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-FMTS = ("int4", "mxfp4", "nvfp4")
-EXACT = {"int4": False, "mxfp4": True, "nvfp4": False}
+FMTS = ("int4", "mxfp4", "nvfp4", "int4_zp")
+EXACT = {"int4": False, "mxfp4": True, "nvfp4": False, "int4_zp": False}
 
 
 def quantized(w_bf16, fmt, layout="rows"):

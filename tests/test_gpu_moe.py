@@ -100,7 +100,7 @@ def _check_layer(out, ref, what):
 
 
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
-@pytest.mark.parametrize("fmt", ("mxfp4", "int4", "nvfp4"))
+@pytest.mark.parametrize("fmt", ("mxfp4", "int4", "nvfp4", "int4_zp"))
 def test_moe_layer_small(fmt, layout):
     E, I, K, T, k = 8, 512, 1024, 37, 2
     log("moe layer", fmt, layout, E, I, K, T, k)
@@ -143,7 +143,7 @@ def test_moe_layer_expert_shape():
     _check_layer(out[tokens], ref, "moe layer 2048x7168")
 
 
-@pytest.mark.parametrize("fmt", ("mxfp4", "int4", "nvfp4"))
+@pytest.mark.parametrize("fmt", ("mxfp4", "int4", "nvfp4", "int4_zp"))
 @pytest.mark.parametrize("E,I,K,T,k", [(8, 512, 1024, 37, 2), (4, 272, 512, 300, 2)])
 def test_grouped_gemm_swiglu(fmt, E, I, K, T, k):
     """The fused gate/up + SwiGLU epilogue against the oracle's grouped GEMM

@@ -11,7 +11,7 @@ from w4_gemm_amd import workloads
 from q4_helpers import assert_quant_equal, log, to_f32
 
 pytestmark = pytest.mark.gpu
-FMTS = ("int4", "mxfp4", "nvfp4")
+FMTS = ("int4", "mxfp4", "nvfp4", "int4_zp")
 DEV = "cuda:0"
 
 
@@ -74,8 +74,8 @@ def test_quantize_all_bf16_values(fmt, layout):
     bits = np.arange(0, 1 << 16, dtype=np.uint32)
     v = (bits << 16).view(np.float32)
     v = v[np.isfinite(v)]
-    if fmt == "int4":
-        v = v[np.abs(v) < 4e5]  # fp16 scale range (|w| < 7*65504)
+    if fmt in ("int4", "int4_zp"):
+        v = v[np.abs(v) < 4e5]  # fp16 scale range (|w| < 7*65504; (hi - lo)/15 < 65504)
     rng = np.random.default_rng(12)
     for order in ("sorted", "shuffled", "mixed"):
         x = v.copy()
@@ -122,7 +122,7 @@ def test_quantize_edge_blocks(fmt, layout):
     w[5, 7] = 1.0                        # one nonzero per block
     w[6, :] = np.linspace(-1, 1, 512)
     w[7, :] = 448.0 * 6 * np.sign(np.linspace(-1, 1, 512))
-    if fmt == "int4":
+    if fmt in ("int4", "int4_zp"):
         w[3] = 0.0
         w[7] = np.sign(w[7]) * 1000.0
     wt = torch.from_numpy(w).to(torch.bfloat16)

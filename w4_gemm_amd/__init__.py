@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
+    "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "INT4_ZP", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
@@ -26,11 +26,11 @@ __all__ = [
     "empty_q4", "quantize", "LIB_PATH",
 ]
 
-INT4_G128, MXFP4, NVFP4, FP8_ROW = 0, 1, 2, 3
-FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4, "fp8_row": FP8_ROW}
+INT4_G128, MXFP4, NVFP4, FP8_ROW, INT4_ZP = 0, 1, 2, 3, 4
+FORMAT_NAMES = {"int4": INT4_G128, "mxfp4": MXFP4, "nvfp4": NVFP4, "fp8_row": FP8_ROW, "int4_zp": INT4_ZP}
 LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 LAYOUT_NAMES = {"rows": LAYOUT_ROWS, "tiled": LAYOUT_TILED}
-GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16, FP8_ROW: 16}
+GROUP = {INT4_G128: 128, MXFP4: 32, NVFP4: 16, FP8_ROW: 16, INT4_ZP: 128}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libq4.so")
@@ -187,13 +187,13 @@ def empty_q4(fmt, rows: int, cols: int, device="cuda", layout=LAYOUT_ROWS) -> Q4
         return Q4Tensor(f, rows, cols, codes, torch.empty(rows, dtype=torch.float32, device=device),
                         None, lay)
     g = GROUP[f]
-    sdt = torch.int16 if f == INT4_G128 else torch.uint8
+    sdt = torch.int16 if f == INT4_G128 else torch.int32 if f == INT4_ZP else torch.uint8
     if lay == LAYOUT_ROWS:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
         scales = torch.empty((rows, cols // g), dtype=sdt, device=device)
     else:
         codes = torch.empty(cb, dtype=torch.uint8, device=device)
-        scales = torch.empty(sb // (2 if f == INT4_G128 else 1), dtype=sdt, device=device)
+        scales = torch.empty(sb // torch.tensor([], dtype=sdt).element_size(), dtype=sdt, device=device)
     gs = torch.empty(1, dtype=torch.float32, device=device) if f == NVFP4 else None
     return Q4Tensor(f, rows, cols, codes, scales, gs, lay)
 

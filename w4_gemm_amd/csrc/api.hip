@@ -19,6 +19,7 @@ int block_of(int fmt) {
     case Q4_MXFP4: return 32;
     case Q4_NVFP4: return 16;
     case Q4_FP8_ROW: return 16;  // row-major rows are stored in 16-byte pieces
+    case Q4_INT4_ZP_G128: return 128;
     default: return 0;
   }
 }
@@ -110,7 +111,8 @@ q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* code
     return Q4_OK;
   }
   if (codes_bytes) *codes_bytes = srows * (size_t)cols / 2;
-  if (scales_bytes) *scales_bytes = srows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : 1);
+  if (scales_bytes)
+    *scales_bytes = srows * (size_t)(cols / g) * (fmt == Q4_INT4_G128 ? 2 : fmt == Q4_INT4_ZP_G128 ? 4 : 1);
   return Q4_OK;
 }
 

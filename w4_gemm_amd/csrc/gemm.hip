@@ -117,6 +117,8 @@ w4a16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t T,
         const int64_t so = scale_off<FMT, LAYOUT>(wrow[nt], k0, K);
         if constexpr (FMT == 0)
           sraw[nt] = reinterpret_cast<const uint16_t*>(scales)[so];
+        else if constexpr (FMT == 4)
+          sraw[nt] = reinterpret_cast<const uint32_t*>(scales)[so];
         else if constexpr (FMT == 1)
           sraw[nt] = reinterpret_cast<const uint8_t*>(scales)[so];
         else  // the lane's two 16-blocks are adjacent in both layouts
@@ -136,6 +138,10 @@ w4a16_kernel(const uint16_t* __restrict__ A, int64_t lda, int64_t T,
           bf16x8_t wb;
           if constexpr (FMT == 0) {
             wb = dq8_int4(wq[nt][i], fp16_value(sraw[nt]));
+          } else if constexpr (FMT == 4) {
+            float sc, off;
+            int4zp_scale(sraw[nt], sc, off);
+            wb = dq8_int4_off(wq[nt][i], sc, off);
           } else if constexpr (FMT == 1) {
             wb = dq8_e2m1(wq[nt][i], e8m0_value(sraw[nt]));
           } else {
@@ -261,6 +267,8 @@ hipError_t dispatch_fmt(int fmt, const uint16_t* A, int64_t lda, int64_t T, cons
     return run_w4a16<0, LAYOUT>(A, lda, T, gather, offsets, gy, M, codes, scales, gs, N, K, C, ldc, stream);
   if (fmt == 1)
     return run_w4a16<1, LAYOUT>(A, lda, T, gather, offsets, gy, M, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 4)
+    return run_w4a16<4, LAYOUT>(A, lda, T, gather, offsets, gy, M, codes, scales, gs, N, K, C, ldc, stream);
   return run_w4a16<2, LAYOUT>(A, lda, T, gather, offsets, gy, M, codes, scales, gs, N, K, C, ldc, stream);
 }
 

@@ -121,14 +121,14 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
   // this lane's scale bytes of a scale group for weight tile jj: MXFP4 4
   // bytes (one per super-chunk), NVFP4 8 (two per super-chunk), INT4 4 fp16
   // of row n = lane%16 (one per super-chunk)
-  constexpr int SW = FMT == 1 ? 1 : 2;  // 32-bit words per tile and group
+  constexpr int SW = FMT == 1 ? 1 : FMT == 4 ? 4 : 2;  // 32-bit words per tile and group
   const uint8_t* ssrc[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int64_t t = min(wt0 + jj, RTW - 1);
-    ssrc[jj] = scales + t * Q * (FMT == 0 ? 128 : FMT == 1 ? 256 : 512);
+    ssrc[jj] = scales + t * Q * (FMT == 0 ? 128 : FMT == 1 || FMT == 4 ? 256 : 512);
   }
-  const int slane = FMT == 0 ? (lane & 15) * 8 : FMT == 1 ? lane * 4 : lane * 8;
+  const int slane = FMT == 0 ? (lane & 15) * 8 : FMT == 4 ? (lane & 15) * 16 : FMT == 1 ? lane * 4 : lane * 8;
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
 
   // scale words of the current scale group and of the next one (loaded
@@ -152,6 +152,10 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
       for (int jj = 0; jj < 4; ++jj) {
         if constexpr (SW == 1) {
           snext[jj][0] = *reinterpret_cast<const uint32_t*>(ssrc[jj] + (int64_t)q * 256 + slane);
+        } else if constexpr (SW == 4) {
+          const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(ssrc[jj] + (int64_t)q * 256 + slane);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) snext[jj][w] = w4[w];
         } else {
           const uint2 w2 = *reinterpret_cast<const uint2*>(ssrc[jj] + (int64_t)q * (FMT == 0 ? 128 : 512) + slane);
           snext[jj][0] = w2.x;
@@ -197,6 +201,10 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
         if constexpr (FMT == 0) {
           const uint32_t hw = (scur[jj][SI >> 1] >> (16 * (SI & 1))) & 0xFFFFu;
           wb[jj] = dq8_int4(wq[jj][i], fp16_value(hw));
+        } else if constexpr (FMT == 4) {
+          float sc, off;
+          int4zp_scale(scur[jj][SI], sc, off);
+          wb[jj] = dq8_int4_off(wq[jj][i], sc, off);
         } else if constexpr (FMT == 1) {
           wb[jj] = dq8_e2m1(wq[jj][i], e8m0_value((scur[jj][0] >> (8 * SI)) & 0xFFu));
         } else {
@@ -275,6 +283,7 @@ hipError_t launch_gemm_w4a16_tiled(int fmt, const uint8_t* codes, const void* sc
   if (M == 0 || N == 0) return hipSuccess;
   if (fmt == 0) return run<0>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
   if (fmt == 1) return run<1>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 4) return run<4>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
   return run<2>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
 }
 

@@ -51,7 +51,7 @@ constexpr int kStepK = kSCS * 128;   // k per step
 // raw scale words (row-major: one per super-chunk; tiled: one q group).
 template <int FMT, int LAYOUT>
 struct StepFrag {
-  static constexpr int NSW = LAYOUT == kLayoutRows ? kSCS : (FMT == 1 ? kSCS / 4 : kSCS / 2);
+  static constexpr int NSW = LAYOUT == kLayoutRows ? kSCS : (FMT == 1 ? kSCS / 4 : FMT == 4 ? kSCS : kSCS / 2);
   u32x4_t w[kSCS];
   uint32_t sw[NSW];
 };
@@ -75,7 +75,7 @@ struct TileStream {
       wbase = codes + (int64_t)n * (K >> 1) + grp * 16;
       wstep = 64;
       sbase = reinterpret_cast<const uint8_t*>(scales) +
-              (int64_t)n * (K / FmtTraits<FMT>::G) * (FMT == 0 ? 2 : 1);
+              (int64_t)n * (K / FmtTraits<FMT>::G) * (FMT == 0 ? 2 : FMT == 4 ? 4 : 1);
       if constexpr (FMT == 1) sbase += grp;        // the lane's block in a super-chunk
       if constexpr (FMT == 2) sbase += 2 * grp;    // the lane's two 16-blocks
     } else {
@@ -84,6 +84,8 @@ struct TileStream {
       wstep = 1024;
       if constexpr (FMT == 0)
         sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 16 + col) * 8;
+      else if constexpr (FMT == 4)
+        sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 16 + col) * 16;
       else if constexpr (FMT == 1)
         sbase = reinterpret_cast<const uint8_t*>(scales) + ((int64_t)tile * Q * 64 + lane) * 4;
       else
@@ -99,6 +101,7 @@ struct TileStream {
       f.w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wbase + sc * wstep));
       if constexpr (LAYOUT == kLayoutRows) {
         if constexpr (FMT == 0) f.sw[c] = reinterpret_cast<const uint16_t*>(sbase)[sc];
+        else if constexpr (FMT == 4) f.sw[c] = reinterpret_cast<const uint32_t*>(sbase)[sc];
         else if constexpr (FMT == 1) f.sw[c] = sbase[sc * 4];
         else f.sw[c] = *reinterpret_cast<const uint16_t*>(sbase + sc * 8);
       }
@@ -109,6 +112,12 @@ struct TileStream {
         const int q = min((kSCS / 4) * st + h, nq - 1);
         if constexpr (FMT == 1) {
           f.sw[h] = reinterpret_cast<const uint32_t*>(sbase)[q * 64];
+        } else if constexpr (FMT == 4) {  // four 32-bit words per row and q group
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sbase + (int64_t)q * 256);
+          f.sw[4 * h] = v[0];
+          f.sw[4 * h + 1] = v[1];
+          f.sw[4 * h + 2] = v[2];
+          f.sw[4 * h + 3] = v[3];
         } else {
           const int stride = FMT == 0 ? 16 * 8 : 64 * 8;  // bytes per q group
           const uint2 v = *reinterpret_cast<const uint2*>(sbase + (int64_t)q * stride);
@@ -124,7 +133,7 @@ struct TileStream {
 // NVFP4 the two E4M3 bytes of the lane's 32 k (first block low); INT4 fp16.
 template <int FMT, int LAYOUT>
 __device__ __forceinline__ uint32_t step_scale(const StepFrag<FMT, LAYOUT>& f, int c) {
-  if constexpr (LAYOUT == kLayoutRows) return f.sw[c];
+  if constexpr (LAYOUT == kLayoutRows || FMT == 4) return f.sw[c];
   else if constexpr (FMT == 1) return (f.sw[c >> 2] >> (8 * (c & 3))) & 0xFFu;
   else return (f.sw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
 }
@@ -149,6 +158,10 @@ __device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW],
         bf16x8_t wb;
         if constexpr (FMT == 0) {
           wb = dq8_int4(f[t].w[c][i], fp16_value(sb[t]));
+        } else if constexpr (FMT == 4) {
+          float s, off;
+          int4zp_scale(sb[t], s, off);
+          wb = dq8_int4_off(f[t].w[c][i], s, off);
         } else if constexpr (FMT == 1) {
           wb = dq8_e2m1(f[t].w[c][i], e8m0_value(sb[t]));
         } else {
@@ -316,6 +329,7 @@ hipError_t launch_gemv(int fmt, int layout, const uint8_t* codes, const void* sc
   if (N == 0 || B == 0) return hipSuccess;
   if (fmt == 0) return dispatch<0>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
   if (fmt == 1) return dispatch<1>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
+  if (fmt == 4) return dispatch<4>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
   return dispatch<2>(layout, codes, scales, gs, N, K, x, ldx, B, y, ldy, stream);
 }
 

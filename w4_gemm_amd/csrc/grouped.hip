@@ -87,7 +87,7 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // raw scale words of one weight tile for one group of four super-chunks
 template <int FMT>
 struct ScaleW {
-  static constexpr int NSW = FMT == 1 ? 1 : 2;
+  static constexpr int NSW = FMT == 1 ? 1 : FMT == 4 ? 4 : 2;
   uint32_t w[NSW];
 };
 
@@ -126,6 +126,7 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
     const int64_t gt = (int64_t)e * NT + min(tile0 + t, NT - 1);
     wsrc[t] = codes + gt * S * 1024;
     if constexpr (FMT == 0) ssrc[t] = scales + (gt * Q * 16 + (lane & 15)) * 8;
+    else if constexpr (FMT == 4) ssrc[t] = scales + (gt * Q * 16 + (lane & 15)) * 16;
     else if constexpr (FMT == 1) ssrc[t] = scales + (gt * Q * 64 + lane) * 4;
     else ssrc[t] = scales + (gt * Q * 64 + lane) * 8;
   }
@@ -142,6 +143,10 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
     for (int t = 0; t < kTPW; ++t) {
       if constexpr (FMT == 1) {
         snext[t].w[0] = *reinterpret_cast<const uint32_t*>(ssrc[t] + (int64_t)q * 256);
+      } else if constexpr (FMT == 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ssrc[t] + (int64_t)q * 256);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) snext[t].w[w] = v[w];
       } else {
         const uint2 v = *reinterpret_cast<const uint2*>(ssrc[t] + (int64_t)q * (FMT == 0 ? 128 : 512));
         snext[t].w[0] = v.x;
@@ -202,6 +207,10 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
           if constexpr (FMT == 0) {
             const uint32_t h = (scur[t].w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
             wb[t] = dq8_int4(wv[t][i], fp16_value(h));
+          } else if constexpr (FMT == 4) {
+            float sc, off;
+            int4zp_scale(scur[t].w[j], sc, off);
+            wb[t] = dq8_int4_off(wv[t][i], sc, off);
           } else if constexpr (FMT == 1) {
             wb[t] = dq8_e2m1(wv[t][i], e8m0_value((scur[t].w[0] >> (8 * j)) & 0xFFu));
           } else {
@@ -335,6 +344,7 @@ hipError_t launch_grouped_tiled(int fmt, const uint16_t* A, int64_t lda, int64_t
   if (E == 0 || N == 0 || P == 0) return hipSuccess;
   if (fmt == 0) return run<0, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
   if (fmt == 1) return run<1, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
+  if (fmt == 4) return run<4, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
   return run<2, false>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N, K, C, ldc, stream);
 }
 
@@ -345,6 +355,7 @@ hipError_t launch_grouped_tiled_swiglu(int fmt, const uint16_t* A, int64_t lda, 
   if (E == 0 || N2 == 0 || P == 0) return hipSuccess;
   if (fmt == 0) return run<0, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
   if (fmt == 1) return run<1, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
+  if (fmt == 4) return run<4, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
   return run<2, true>(A, lda, T, gather, offsets, E, P, codes, scales, gs, N2, K, H, ldh, stream);
 }
 

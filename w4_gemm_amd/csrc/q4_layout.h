@@ -14,7 +14,7 @@ constexpr int kLayoutTiled = 1;
 
 template <int FMT>
 struct FmtTraits {
-  static constexpr int G = FMT == 0 ? 128 : (FMT == 1 ? 32 : 16);  // block size along K
+  static constexpr int G = (FMT == 0 || FMT == 4) ? 128 : (FMT == 1 ? 32 : 16);  // block size along K
 };
 
 // Byte offset of the 4 code bytes holding elements k0..k0+7 (k0 % 8 == 0)
@@ -39,7 +39,7 @@ __host__ __device__ __forceinline__ int64_t scale_off(int64_t r, int64_t k, int6
   } else {
     const int64_t Q = K >> 9;
     const int64_t t = r >> 4, n = r & 15, s = k >> 7, q = s >> 2, i = s & 3;
-    if constexpr (FMT == 0) {
+    if constexpr (FMT == 0 || FMT == 4) {  // fp16 scales / 32-bit scale + zero-point words
       return (((t * Q + q) << 4) + n) * 4 + i;
     } else {
       const int64_t g = (k >> 5) & 3;

@@ -56,14 +56,14 @@ __device__ __forceinline__ bf16x8_t dq8_e2m1_mul(uint32_t w, float scale) {
   return as_bf16x8(r);
 }
 
-// 8 INT4 codes (two's complement nibbles) times fp32 scale s -> 8 bf16.
+// 8 INT4 codes (two's complement nibbles) -> 8 bf16 of (q + 8) * s + off.
 // Offset-binary trick: nibble ^ 8 = q + 8 in 0..15, read as a byte by
-// v_cvt_f32_ubyte; q*s = (q+8)*s - 8*s is exact in fp32 (<= 15 bits), so
-// one fma gives it; then one rounding to bf16.
-__device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) {
+// v_cvt_f32_ubyte; with off = -(8 + z) * s this is (q - z) * s, exact in
+// fp32 (<= 15 bits), so one fma gives it; then one rounding to bf16.
+// Symmetric INT4: z = 0; INT4 with a zero point: z from the group's word.
+__device__ __forceinline__ bf16x8_t dq8_int4_off(uint32_t w, float s, float m8) {
   const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // elements 0,2,4,6
   const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // elements 1,3,5,7
-  const float m8 = -8.0f * s;
   u32x4_t r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -72,6 +72,15 @@ __device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) {
     r[j] = pk_bf16(e0, e1);
   }
   return as_bf16x8(r);
+}
+
+__device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) { return dq8_int4_off(w, s, -8.0f * s); }
+
+// INT4 with a zero point: the group's 32-bit word (fp16 scale, int8 zero
+// point in bits 16..23) -> (scale, offset) for dq8_int4_off.
+__device__ __forceinline__ void int4zp_scale(uint32_t word, float& s, float& off) {
+  s = fp16_value(word & 0xFFFFu);
+  off = -(float)(8 + (int)(int8_t)((word >> 16) & 0xFFu)) * s;
 }
 
 // bf16 matrix core: C(16x16) += A(16x32) * B(32x16), fp32 accumulation.

@@ -12,6 +12,11 @@
 //   NVFP4      gs = max(amax_tensor,1e-12)/2688; block code
 //              E4M3(min((amax_b/6)/gs, 448)); code = E2M1(clamp(w/(E4M3*gs)))
 //              (same file, nvfp4)
+//   INT4 + zero point, g128 (format cheat sheet, W4A16 INT4 GPTQ/AWQ row:
+//              integers -8..7, one scale per 128, plus a zero point; min-max
+//              rounding): lo = min(min, 0), hi = max(max, 0),
+//              s = fp16((hi - lo)/15), z = clamp(-8 - rne(lo/s), -8, 7),
+//              code = clamp(rne(w/s) + z, -8, 7); word = fp16 s | z << 16
 //
 // Launch shape: one lane per 8 consecutive values of a row (one 16-byte
 // load, one 4-byte store of packed nibbles at the position the layout
@@ -68,6 +73,53 @@ __device__ __forceinline__ float group_max(float a) {
   return a;
 }
 
+template <int LANES>
+__device__ __forceinline__ float group_min(float a) {
+#pragma unroll
+  for (int m = 1; m < LANES; m <<= 1) a = fminf(a, __shfl_xor(a, m));
+  return a;
+}
+
+__device__ __forceinline__ float min8(const Chunk8& c) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fminf(a, c.v[j]);
+  return a;
+}
+
+__device__ __forceinline__ float max8(const Chunk8& c) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, c.v[j]);
+  return a;
+}
+
+// INT4 with a zero point: the group's scale word and (s, z) from its range
+// [lo, hi] (already widened to include 0).
+struct ZpParams {
+  uint32_t word;
+  float s, z;
+};
+__device__ __forceinline__ ZpParams int4zp_params(float lo, float hi) {
+  const uint32_t sbits = fp16_encode((hi - lo) / 15.0f);
+  const float s = fp16_value(sbits);
+  if (s == 0.0f) return ZpParams{0u, 0.0f, 0.0f};
+  const float z = fminf(fmaxf(-8.0f - __builtin_rintf(lo / s), -8.0f), 7.0f);
+  return ZpParams{sbits | (((uint32_t)(int)z & 0xFFu) << 16), s, z};
+}
+
+// Eight values -> eight INT4 nibbles with the zero point (codes 0 if s == 0).
+__device__ __forceinline__ uint32_t int4zp_pack8(const Chunk8& c, const ZpParams& zp) {
+  uint32_t p = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int qv = 0;
+    if (zp.s != 0.0f) qv = (int)fminf(fmaxf(__builtin_rintf(c.v[j] / zp.s) + zp.z, -8.0f), 7.0f);
+    p |= ((uint32_t)qv & 0xFu) << (4 * j);
+  }
+  return p;
+}
+
 __device__ __forceinline__ float absmax8(const Chunk8& c) {
   float a = 0.0f;
 #pragma unroll
@@ -107,7 +159,7 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
     const int64_t k0 = valid ? (c - r * cpr) * 8 : 0;
     const bool in_src = valid && r < rows;  // tiled padding rows read as zeros
     Chunk8 x = load8(src + (in_src ? r * ld + k0 : 0), in_src);
-    const float amax = group_max<LANES>(absmax8(x));
+    const float amax = FMT == 4 ? 0.0f : group_max<LANES>(absmax8(x));
 
     uint32_t packed = 0;
     if constexpr (FMT == 0) {
@@ -125,6 +177,11 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
       }
       if (valid && (k0 % G) == 0)
         reinterpret_cast<uint16_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint16_t)sbits;
+    } else if constexpr (FMT == 4) {
+      const ZpParams zp = int4zp_params(group_min<LANES>(min8(x)), group_max<LANES>(max8(x)));
+      packed = int4zp_pack8(x, zp);
+      if (valid && (k0 % G) == 0)
+        reinterpret_cast<uint32_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = zp.word;
     } else if constexpr (FMT == 1) {
       const uint32_t e = mx_e8m0(amax);
       packed = e2m1_pack8(x, e8m0_value(e));
@@ -232,6 +289,21 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
       uint16_t* sp = reinterpret_cast<uint16_t*>(scales);
       if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 16 + n) * 4 + si] = (uint16_t)sbits;
       else sp[r * S + s] = (uint16_t)sbits;
+    }
+  } else if constexpr (FMT == 4) {
+    float lo = fminf(fminf(min8(x[0]), min8(x[1])), fminf(min8(x[2]), min8(x[3])));
+    float hi = fmaxf(fmaxf(max8(x[0]), max8(x[1])), fmaxf(max8(x[2]), max8(x[3])));
+    lo = fminf(lo, __shfl_xor(lo, 16));
+    lo = fminf(lo, __shfl_xor(lo, 32));
+    hi = fmaxf(hi, __shfl_xor(hi, 16));
+    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    const ZpParams zp = int4zp_params(lo, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) packed[i] = int4zp_pack8(x[i], zp);
+    if (store && g == 0) {
+      uint32_t* sp = reinterpret_cast<uint32_t*>(scales);
+      if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 16 + n) * 4 + si] = zp.word;
+      else sp[r * S + s] = zp.word;
     }
   } else if constexpr (FMT == 1) {
     const float amax = fmaxf(fmaxf(absmax8(x[0]), absmax8(x[1])), fmaxf(absmax8(x[2]), absmax8(x[3])));
@@ -346,6 +418,15 @@ dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scale
         const int q = ((int)(packed << (28 - 4 * j))) >> 28;  // sign-extend nibble j
         v[j] = (float)q * s;
       }
+    } else if constexpr (FMT == 4) {
+      const uint32_t word = reinterpret_cast<const uint32_t*>(scales)[si];
+      const float s = fp16_value(word & 0xFFFFu);
+      const int z = (int)(int8_t)((word >> 16) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = ((int)(packed << (28 - 4 * j))) >> 28;
+        v[j] = (float)(q - z) * s;
+      }
     } else if constexpr (FMT == 1) {
       const float s = e8m0_value(reinterpret_cast<const uint8_t*>(scales)[si]);
 #pragma unroll
@@ -400,6 +481,8 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
   const int64_t chunks = stored_rows<LAYOUT>(rows) * (cols >> 3);
   if (fmt == 0) {
     if (chunks) launch_q<0, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
+  } else if (fmt == 4) {
+    if (chunks) launch_q<4, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
   } else if (fmt == 1) {
     if (chunks) launch_q<1, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
   } else {
@@ -436,9 +519,9 @@ hipError_t dequant_layout(int fmt, const uint8_t* codes, const void* scales, con
   const unsigned grid = grid_for(chunks);
 #define Q4_DQ(F, O) dequant_kernel<F, O, LAYOUT><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
   if (dst_dtype == 0) {
-    if (fmt == 0) Q4_DQ(0, 0); else if (fmt == 1) Q4_DQ(1, 0); else Q4_DQ(2, 0);
+    if (fmt == 0) Q4_DQ(0, 0); else if (fmt == 1) Q4_DQ(1, 0); else if (fmt == 4) Q4_DQ(4, 0); else Q4_DQ(2, 0);
   } else {
-    if (fmt == 0) Q4_DQ(0, 1); else if (fmt == 1) Q4_DQ(1, 1); else Q4_DQ(2, 1);
+    if (fmt == 0) Q4_DQ(0, 1); else if (fmt == 1) Q4_DQ(1, 1); else if (fmt == 4) Q4_DQ(4, 1); else Q4_DQ(2, 1);
   }
 #undef Q4_DQ
   return hipGetLastError();
