@@ -55,6 +55,36 @@ def test_gemv_small(fmt, N, K, layout):
         check_matmul(yc[:, :N], ref, to_f32(x), wd, EXACT[fmt], f"gemv {fmt} B={B}")
 
 
+def tiny_rows(N, K, seed):
+    """Weights whose rows span many magnitudes (row n scaled by 10^-(n % 6)):
+    INT4 groups of the small rows get fp16-subnormal scales, NVFP4 blocks
+    E4M3-subnormal scales, MXFP4 blocks small E8M0 exponents."""
+    w = workloads.matrix(f"tg/tiny{N}x{K}", N, K, 0.02, seed=seed).float()
+    w *= torch.tensor([10.0 ** -(n % 6) for n in range(N)]).reshape(N, 1)
+    return w.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_tiny_scales(fmt, layout):
+    N, K = 96, 1024
+    w = tiny_rows(N, K, 28)
+    qg, qr = quantized(w, fmt, layout)
+    wd = oracle.dequant(qr)
+    sc = np.asarray(qr.scales).astype(np.int64).ravel()   # the case is really there
+    if fmt in ("int4", "int4_zp"):
+        assert np.any(((sc & 0x7C00) == 0) & ((sc & 0x3FF) != 0))    # fp16 subnormal
+    elif fmt == "nvfp4":
+        assert np.any(((sc & 0x78) == 0) & ((sc & 0x7) != 0))        # E4M3 subnormal
+    for B in (1, 16):
+        x = workloads.matrix(f"tg/tinyx{B}", B, K, 1.0, seed=29)
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemv(qg, x.to(DEV), y)
+        torch.cuda.synchronize()
+        check_matmul(y.cpu(), oracle.matmul_f64(to_f32(x), wd), to_f32(x), wd, EXACT[fmt],
+                     f"gemv tiny {fmt} B={B}")
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemv_one_hot_x_returns_a_column(fmt, layout):
@@ -178,6 +208,20 @@ def test_gemm_w4a16_small(fmt, M, N, K, layout):
     wd = oracle.dequant(qr)
     check_matmul(Cc[:, :N], oracle.matmul_f64(to_f32(a), wd), to_f32(a), wd, EXACT[fmt],
                  f"w4a16 {fmt}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_w4a16_tiny_scales(fmt, layout):
+    M, N, K = 70, 96, 1024
+    w = tiny_rows(N, K, 30)
+    a = workloads.matrix("tm/tinya", M, K, 1.0, seed=34)
+    qg, qr = quantized(w, fmt, layout)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    q4.q4_gemm(a.to(DEV), qg, C)
+    torch.cuda.synchronize()
+    wd = oracle.dequant(qr)
+    check_matmul(C.cpu(), oracle.matmul_f64(to_f32(a), wd), to_f32(a), wd, EXACT[fmt], f"w4a16 tiny {fmt}")
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)

@@ -31,9 +31,18 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-file flags.  The GEMV applies its INT4 group scales with VALU
+# instructions to matrix-core results; writing those results to ordinary
+# VGPRs saves a v_accvgpr_read per value (its accumulators are few, so the
+# 256-register limit of that form is no constraint there).
+FILE_FLAGS = {
+    "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -106,11 +106,6 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// fp16 bits -> fp32 (v_cvt_f32_f16, exact).
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
@@ -203,7 +198,7 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
     i32x8_t wq[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      sw[jj] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(
+      sw[jj] = fp16_value(*reinterpret_cast<const uint16_t*>(
           &sbuf[(s >> 2) & 1][(wn * 4 + jj) * 128 + (lane & 15) * 8 + j * 2]));
       wq[jj] = int4_frag_to_e4m3(*reinterpret_cast<const u32x4_t*>(&wbuf[bi][wn * 4 + jj][lane * 16]));
     }

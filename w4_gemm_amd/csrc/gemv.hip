@@ -138,12 +138,53 @@ __device__ __forceinline__ uint32_t step_scale(const StepFrag<FMT, LAYOUT>& f, i
   else return (f.sw[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
 }
 
-// Dequantize one step of TPW tiles and multiply them by x read from LDS at
-// xrow (this lane's batch row, already offset to the step and to the lane's
-// 32 k); each x fragment feeds every tile.
+// INT4 with or without a zero point.  A 128-wide group is one super-chunk,
+// so the four matrix steps of a super-chunk share one scale (and zero
+// point) per output column n, and the scale can be applied after them: the
+// steps multiply x (staged in LDS in the order of dq8_int4_biased) by the
+// exact bf16 values 128 + q + 8, a fifth product of x with ones gives the
+// group's sum X of x per batch row, and the group adds
+//   s * (P - (136 + z) * X) = s * sum_k x_k (q_k - z)
+// to the fp32 accumulator.  The products are exact; the only roundings are
+// fp32 sums (about 2^-17 of sum |x w'| here, against 2^-9 when w' is first
+// rounded to bf16), and the VALU work per code drops from about three
+// instructions to one.
 template <int FMT, int LAYOUT, int TPW>
-__device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW], const uint16_t* xrow,
-                                          bool xlane, float gs, f32x4_t (&acc)[TPW][2]) {
+__device__ __forceinline__ void step_math_int4(const StepFrag<FMT, LAYOUT> (&f)[TPW], const uint16_t* xrow,
+                                               f32x4_t (&acc)[TPW][2]) {
+  const bf16x8_t ones = as_bf16x8(u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+  for (int c = 0; c < kSCS; ++c) {
+    f32x4_t xsum = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t p[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) p[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xrow + c * 128 + 8 * i);
+      xsum = mma16x16x32(as_bf16x8(xv), ones, xsum);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) p[t] = mma16x16x32(as_bf16x8(xv), dq8_int4_biased(f[t].w[c][i]), p[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const uint32_t sb = step_scale<FMT, LAYOUT>(f[t], c);
+      const float s = fp16_value(sb & 0xFFFFu);
+      const float kz = FMT == 4 ? -(float)(136 + (int)(int8_t)((sb >> 16) & 0xFFu)) : -136.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[t][c & 1][r] = __builtin_fmaf(s, __builtin_fmaf(kz, xsum[r], p[t][r]), acc[t][c & 1][r]);
+    }
+  }
+}
+
+// MXFP4 / NVFP4: dequantize one step of TPW tiles to bf16 and multiply them
+// by x read from LDS at xrow (this lane's batch row, already offset to the
+// step and to the lane's 32 k; a row of zeros for lanes past the batch);
+// each x fragment feeds every tile.
+template <int FMT, int LAYOUT, int TPW>
+__device__ __forceinline__ void step_math_fp4(const StepFrag<FMT, LAYOUT> (&f)[TPW], const uint16_t* xrow,
+                                              float gs, f32x4_t (&acc)[TPW][2]) {
 #pragma unroll
   for (int c = 0; c < kSCS; ++c) {
     uint32_t sb[TPW];
@@ -151,18 +192,11 @@ __device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW],
     for (int t = 0; t < TPW; ++t) sb[t] = step_scale<FMT, LAYOUT>(f[t], c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4_t xv = xlane ? *reinterpret_cast<const u32x4_t*>(xrow + c * 128 + 8 * i)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xrow + c * 128 + 8 * i);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         bf16x8_t wb;
-        if constexpr (FMT == 0) {
-          wb = dq8_int4(f[t].w[c][i], fp16_value(sb[t]));
-        } else if constexpr (FMT == 4) {
-          float s, off;
-          int4zp_scale(sb[t], s, off);
-          wb = dq8_int4_off(f[t].w[c][i], s, off);
-        } else if constexpr (FMT == 1) {
+        if constexpr (FMT == 1) {
           wb = dq8_e2m1(f[t].w[c][i], e8m0_value(sb[t]));
         } else {
           const uint32_t e = (i < 2) ? (sb[t] & 0xFFu) : (sb[t] >> 8);
@@ -172,6 +206,13 @@ __device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW],
       }
     }
   }
+}
+
+template <int FMT, int LAYOUT, int TPW>
+__device__ __forceinline__ void step_math(const StepFrag<FMT, LAYOUT> (&f)[TPW], const uint16_t* xrow,
+                                          float gs, f32x4_t (&acc)[TPW][2]) {
+  if constexpr (FMT == 0 || FMT == 4) step_math_int4<FMT, LAYOUT, TPW>(f, xrow, acc);
+  else step_math_fp4<FMT, LAYOUT, TPW>(f, xrow, gs, acc);
 }
 
 // lane l, register r of the accumulator holds (b = 4(l/16) + r, n = l%16)
@@ -185,8 +226,9 @@ __device__ __forceinline__ void store_y(f32x4_t acc, int tile, int ntiles, int N
   }
 }
 
-// x staged per step: [2][BT][kStepK + 8] bf16 (+ one spare 16-byte slot).
-// Each wave owns TPW adjacent row tiles.
+// x staged per step: [2][BT][kStepK + 8] bf16, one spare 16-byte slot, and
+// one row of kStepK zeros that the lanes past the batch read (the matrix
+// core always takes 16 rows of x).  Each wave owns TPW adjacent row tiles.
 template <int FMT, int LAYOUT, int BT, int TPW>
 __global__ void __launch_bounds__(kWaves * 64)
 gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
@@ -227,7 +269,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
       const bool ok = pc / (kStepK / 8) < B && st * kStepK + (pc % (kStepK / 8)) * 8 < K;
       uint16_t* dst = p < XPIECES ? &xs[buf][p / (kStepK / 8)][(p % (kStepK / 8)) * 8]
                                   : &xs_raw[2 * BT * XROW];
-      *reinterpret_cast<u32x4_t*>(dst) = ok ? xr[j] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t v = (FMT == 0 || FMT == 4) ? x8_int4_order(xr[j]) : xr[j];
+      *reinterpret_cast<u32x4_t*>(dst) = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
 
@@ -236,8 +279,14 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
   for (int t = 0; t < TPW; ++t)
     ts[t] = TileStream<FMT, LAYOUT>(codes, scales, min(tile + t, ntiles - 1), N, K, lane);
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
+  // the lane's x row: its batch row in the current buffer, or the zero row
+  uint16_t* const xzero = &xs_raw[2 * BT * XROW + 8];
+  if (tid < kStepK / 8) *reinterpret_cast<u32x4_t*>(xzero + 8 * tid) = u32x4_t{0u, 0u, 0u, 0u};
   const bool xlane = col < BT;
-  const int xoff = (xlane ? col : 0) * XROW + grp * 32;
+  const int xoff = col * XROW + grp * 32;
+  auto xrow = [&](int buf) -> const uint16_t* {
+    return xlane ? &xs[buf][0][0] + xoff : xzero + grp * 32;
+  };
   f32x4_t acc[TPW][2];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) acc[t][0] = acc[t][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -267,22 +316,22 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
   int st = 0;
   for (; st + 2 < nst; st += 2) {
     prefetch(fb, st + 1);
-    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
+    step_math<FMT, LAYOUT, TPW>(fa, xrow(st & 1), gs, acc);
     store_x(xr, (st + 1) & 1, st + 1);
     __syncthreads();
     prefetch(fa, st + 2);
-    step_math<FMT, LAYOUT, TPW>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc);
+    step_math<FMT, LAYOUT, TPW>(fb, xrow((st + 1) & 1), gs, acc);
     store_x(xr, st & 1, st + 2);
     __syncthreads();
   }
   if (st + 1 < nst) {  // two steps left
     prefetch(fb, st + 1);
-    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
+    step_math<FMT, LAYOUT, TPW>(fa, xrow(st & 1), gs, acc);
     store_x(xr, (st + 1) & 1, st + 1);
     __syncthreads();
-    step_math<FMT, LAYOUT, TPW>(fb, &xs[(st + 1) & 1][0][0] + xoff, xlane, gs, acc);
+    step_math<FMT, LAYOUT, TPW>(fb, xrow((st + 1) & 1), gs, acc);
   } else {             // one step left
-    step_math<FMT, LAYOUT, TPW>(fa, &xs[st & 1][0][0] + xoff, xlane, gs, acc);
+    step_math<FMT, LAYOUT, TPW>(fa, xrow(st & 1), gs, acc);
   }
 
 #pragma unroll
@@ -296,7 +345,7 @@ hipError_t run(const uint8_t* codes, const void* scales, const float* gs, int64_
   const int64_t ntiles = (N + 15) / 16;
   const int64_t nwaves = (ntiles + TPW - 1) / TPW;
   const unsigned grid = (unsigned)((nwaves + kWaves - 1) / kWaves);
-  const size_t lds = (2ull * BT * (kStepK + 8) + 8) * sizeof(uint16_t);  // + spare slot
+  const size_t lds = (2ull * BT * (kStepK + 8) + 8 + kStepK) * sizeof(uint16_t);  // + spare slot, zero row
   gemv_kernel<FMT, LAYOUT, BT, TPW><<<grid, kWaves * 64, lds, stream>>>(
       codes, scales, gs, (int)N, (int)K, x, ldx, (int)B, y, ldy);
   return hipGetLastError();

@@ -45,11 +45,13 @@ __device__ __forceinline__ uint32_t e4m3_encode(float t) {
   return (u >> 20) - ((127u - 7u) << 3);     // rebias exponent 127 -> 7
 }
 
-// E4M3 code -> fp32 (exact).
+// E4M3 code (sign bit ignored) -> fp32, exact and branch-free: the code's
+// exponent and mantissa bits placed at the top of an fp32 read as
+// 2^(e-127) (1 + m/8), or m 2^-129 for e = 0 (an fp32 subnormal); times
+// 2^120 that is 2^(e-7) (1 + m/8), resp. m 2^-9.  Needs fp32 denormals
+// preserved, which the kernels are built with.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;       // m * 2^-9
-  return u2f(((e + 120u) << 23) | (m << 20));
+  return u2f((c & 0x7Fu) << 20) * 0x1p120f;
 }
 
 // FP16 bits (sign 0) of t >= 0; >= 65520 gives +inf.
@@ -63,15 +65,10 @@ __device__ __forceinline__ uint32_t fp16_encode(float t) {
   return (u >> 13) - ((127u - 15u) << 10);
 }
 
-// FP16 bits -> fp32 (exact, subnormals included).
+// FP16 bits -> fp32: one v_cvt_f32_f16, exact for every fp16 value
+// (subnormals included: the kernels run with fp16 denormals preserved).
 __device__ __forceinline__ float fp16_value(uint32_t h) {
-  uint32_t s = (h & 0x8000u) << 16, e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
-  if (e == 0) {
-    float v = (float)m * 5.9604644775390625e-08f;  // m * 2^-24
-    return s ? -v : v;
-  }
-  if (e == 31) return u2f(s | 0x7F800000u | (m << 13));
-  return u2f(s | ((e + 112u) << 23) | (m << 13));
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
 // MXFP4 scale exponent for a block whose absmax is amax (fp32, >= 0):

@@ -76,6 +76,32 @@ __device__ __forceinline__ bf16x8_t dq8_int4_off(uint32_t w, float s, float m8) 
 
 __device__ __forceinline__ bf16x8_t dq8_int4(uint32_t w, float s) { return dq8_int4_off(w, s, -8.0f * s); }
 
+// 8 INT4 codes -> 8 bf16 of 128 + (q + 8), exact and without the scale (for
+// kernels that apply a group's scale after the matrix step).  bf16 0x4300 is
+// 128 with a last place of 1, so the offset-binary nibble q ^ 8 placed in
+// the four low mantissa bits reads as 128 + q + 8: one bit-select per pair
+// (nibble with its top bit flipped, 0x4300 elsewhere) after a shift.  The
+// pairs are (0,4), (1,5), (2,6), (3,7), so the output holds elements
+// 0,4,1,5,2,6,3,7 -- the other operand must follow that order
+// (x8_int4_order).
+__device__ __forceinline__ bf16x8_t dq8_int4_biased(uint32_t w) {
+  constexpr uint32_t kNib = 0x000F000Fu, kMagic = 0x43084308u;
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v = w >> (4 * j);
+    r[j] = ((v ^ kMagic) & kNib) | (kMagic & ~kNib);
+  }
+  return as_bf16x8(r);
+}
+
+// Eight bf16 in k order (x0..x7) -> the order of dq8_int4_biased:
+// x0,x4,x1,x5,x2,x6,x3,x7 (one byte permute per output dword).
+__device__ __forceinline__ u32x4_t x8_int4_order(u32x4_t v) {
+  return u32x4_t{__builtin_amdgcn_perm(v[2], v[0], 0x05040100u), __builtin_amdgcn_perm(v[2], v[0], 0x07060302u),
+                 __builtin_amdgcn_perm(v[3], v[1], 0x05040100u), __builtin_amdgcn_perm(v[3], v[1], 0x07060302u)};
+}
+
 // INT4 with a zero point: the group's 32-bit word (fp16 scale, int8 zero
 // point in bits 16..23) -> (scale, offset) for dq8_int4_off.
 __device__ __forceinline__ void int4zp_scale(uint32_t word, float& s, float& off) {
