@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 matrix cores
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
+GRAPH_STEPS = 10               # decode steps captured per HIP graph in the timed loop
 METRIC = "W4 GEMV weight GB/s and W4 GEMM TFLOP/s vs MI355X roofline, 1 GPU"
 
 
@@ -162,24 +163,29 @@ def main():
 
     # one step = one GEMV per decode batch; step i uses weight copies
     # 3i, 3i+1, 3i+2 (mod the number of copies), so consecutive launches never
-    # share a copy.  Steps are captured as HIP graphs and replayed.
+    # share a copy.  Steps are captured as HIP graphs and replayed: a graph of
+    # GRAPH_STEPS consecutive steps (a whole number of copy-pattern periods,
+    # as a decode loop captures many kernels per graph) for the bulk of the K
+    # steps, one-step graphs for the remainder and the warmup.
     ncopy = len(copies)
     nb = len(batches)
     period = ncopy // __import__("math").gcd(ncopy, nb)   # steps until the copy pattern repeats
+    graph_steps = period * max(1, GRAPH_STEPS // period)
 
-    def make_step(i):
-        def run(_):
-            for j, b in enumerate(batches):
-                q4.q4_gemv(copies[(i * nb + j) % ncopy], xs[b], ys[b])
-        return run
+    def step(i):
+        for j, b in enumerate(batches):
+            q4.q4_gemv(copies[(i * nb + j) % ncopy], xs[b], ys[b])
 
-    step_graphs = [GraphTimer(torch, make_step(i)) for i in range(period)]
+    step_graphs = [GraphTimer(torch, lambda _, i=i: step(i)) for i in range(period)]
+    bulk = GraphTimer(torch, step, per_graph=graph_steps)
     for i in range(args.warmup):
         step_graphs[i % period].graph.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    for i in range(args.steps):
+    for _ in range(args.steps // graph_steps):
+        bulk.graph.replay()
+    for i in range(args.steps % graph_steps):
         step_graphs[i % period].graph.replay()
     t1.record()
     torch.cuda.synchronize()

@@ -20,8 +20,9 @@
 //     rows.
 //   * each wave owns one tile of 16 rows and walks the whole K in steps of
 //     4 super-chunks (512 k: 4 KB of codes and one 4- or 8-byte scale word
-//     per lane in the tiled layout).  The tiles of a workgroup's 4 waves are
-//     spread over the matrix (tile = wave * workgroups + workgroup).
+//     per lane in the tiled layout).  The tiles of a workgroup's 4 or 8
+//     waves are spread over the matrix (tile = wave * workgroups +
+//     workgroup).
 //   * x is staged in LDS once per step by the whole workgroup (BT rows,
 //     double-buffered) and shared by its waves.  The next step's x loads are
 //     issued first, then its code loads (non-temporal: the weights are
@@ -43,7 +44,6 @@
 namespace q4 {
 namespace {
 
-constexpr int kWaves = 4;            // waves (row tiles) per workgroup
 constexpr int kSCS = 4;              // super-chunks per step
 constexpr int kStepK = kSCS * 128;   // k per step
 
@@ -229,18 +229,18 @@ __device__ __forceinline__ void store_y(f32x4_t acc, int tile, int ntiles, int N
 // x staged per step: [2][BT][kStepK + 8] bf16, one spare 16-byte slot, and
 // one row of kStepK zeros that the lanes past the batch read (the matrix
 // core always takes 16 rows of x).  Each wave owns TPW adjacent row tiles.
-template <int FMT, int LAYOUT, int BT, int TPW>
-__global__ void __launch_bounds__(kWaves * 64)
+template <int FMT, int LAYOUT, int BT, int TPW, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64)
 gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
             const float* __restrict__ gs_ptr, int N, int K,
             const uint16_t* __restrict__ x, int64_t ldx, int B,
             uint16_t* __restrict__ y, int64_t ldy) {
   constexpr int XROW = kStepK + 8;
   constexpr int XPIECES = BT * kStepK / 8;                  // 16-byte pieces per step
-  constexpr int XPER = (XPIECES + 64 * kWaves - 1) / (64 * kWaves);  // per thread
+  constexpr int XPER = (XPIECES + 64 * WAVES - 1) / (64 * WAVES);  // per thread
   extern __shared__ __attribute__((aligned(16))) uint16_t xs_raw[];
   auto xs = reinterpret_cast<uint16_t(*)[BT][XROW]>(xs_raw);
-  constexpr int W = kWaves;
+  constexpr int W = WAVES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int ntiles = (N + 15) >> 4;
@@ -338,15 +338,19 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
   for (int t = 0; t < TPW; ++t) store_y(acc[t][0] + acc[t][1], tile + t, ntiles, N, B, lane, y, ldy);
 }
 
-template <int FMT, int LAYOUT, int BT, int TPW = (BT >= 16 ? 2 : 1)>
+// Launch shape (measured on the 28672 x 8192 decode GEMV): one tile per
+// wave and 8 waves per workgroup -- two waves per SIMD hide the x and
+// weight load latencies that a single wave per SIMD exposes -- except INT4
+// at B = 1, which ran ~4% faster with 4 waves.
+template <int FMT, int LAYOUT, int BT, int TPW = 1, int WAVES = (BT == 1 && (FMT == 0 || FMT == 4)) ? 4 : 8>
 hipError_t run(const uint8_t* codes, const void* scales, const float* gs, int64_t N, int64_t K,
                const uint16_t* x, int64_t ldx, int64_t B, uint16_t* y, int64_t ldy,
                hipStream_t stream) {
   const int64_t ntiles = (N + 15) / 16;
   const int64_t nwaves = (ntiles + TPW - 1) / TPW;
-  const unsigned grid = (unsigned)((nwaves + kWaves - 1) / kWaves);
+  const unsigned grid = (unsigned)((nwaves + WAVES - 1) / WAVES);
   const size_t lds = (2ull * BT * (kStepK + 8) + 8 + kStepK) * sizeof(uint16_t);  // + spare slot, zero row
-  gemv_kernel<FMT, LAYOUT, BT, TPW><<<grid, kWaves * 64, lds, stream>>>(
+  gemv_kernel<FMT, LAYOUT, BT, TPW, WAVES><<<grid, WAVES * 64, lds, stream>>>(
       codes, scales, gs, (int)N, (int)K, x, ldx, (int)B, y, ldy);
   return hipGetLastError();
 }
