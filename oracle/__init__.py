@@ -290,17 +290,27 @@ def gemm_w4a16(a, q: QTensor, rows=None) -> np.ndarray:
 
 
 def gemm_w4a4(a, q: QTensor, rows=None, aq: QTensor | None = None) -> np.ndarray:
-    """W4A4 MXFP4 GEMM: C = deq(mxfp4(A)) deq(W)^T (fp64)."""
-    if q.fmt != "mxfp4":
-        raise ValueError("W4A4 is defined for MXFP4 operands")
+    """W4A4 GEMM: C = deq(fmt(A)) deq(W)^T (fp64), both operands in the
+    weight's FP4 format ("Low-bit inference for very large MoE", table
+    "Kernels on different hardware", row W4A4; "Quantization in deployment",
+    the MXFP4 and NVFP4 rows of the cheat sheet).  MXFP4: E8M0 per 32.
+    NVFP4: E4M3 per 16 and A's own tensor global scale, computed from the
+    whole of A (so a row subset must come with the full-A quantization `aq`,
+    or the full A)."""
+    if q.fmt not in ("mxfp4", "nvfp4"):
+        raise ValueError("W4A4 is defined for MXFP4 and NVFP4 operands")
     if aq is None:
         a = _f32(a)
-        if rows is not None:
-            a = np.ascontiguousarray(a[np.asarray(rows)])
-        aq = quantize("mxfp4", a)
-    elif rows is not None:
-        aq = QTensor("mxfp4", len(rows), aq.cols, aq.codes[np.asarray(rows)],
-                     aq.scales[np.asarray(rows)])
+        if rows is not None and q.fmt == "mxfp4":   # row-local scales: quantize the rows only
+            aq = quantize("mxfp4", np.ascontiguousarray(a[np.asarray(rows)]))
+            rows = None
+        else:
+            aq = quantize(q.fmt, a)
+    if aq.fmt != q.fmt:
+        raise ValueError("W4A4 takes both operands in one format")
+    if rows is not None:
+        aq = QTensor(aq.fmt, len(rows), aq.cols, aq.codes[np.asarray(rows)],
+                     aq.scales[np.asarray(rows)], aq.gs)
     return matmul_f64(dequant(aq), dequant(q))
 
 
