@@ -30,6 +30,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+FP16_PEAK_TFLOPS = 2500.0      # dense fp16 matrix cores (the W4A4 NVFP4 kernel's)
 FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 matrix cores
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
 GRAPH_STEPS = 10               # decode steps captured per HIP graph in the timed loop
@@ -281,6 +282,8 @@ def main():
         extra["moe_grouped_mxfp4_64x2048x7168"] = bench_moe(torch, q4, workloads, dev, args.seed)
     if want("w4a4"):
         extra["w4a4_mxfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed)
+    if want("w4a4_nvfp4"):
+        extra["w4a4_nvfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed, "nvfp4")
     if want("moe_layer"):
         extra["moe_layer_mxfp4_64x(2x2048|7168)"] = bench_moe_layer(torch, q4, workloads, dev, args.seed)
     if want("w4a8"):
@@ -427,21 +430,26 @@ def bench_moe_layer(torch, q4, workloads, dev, seed):
             "steps_us": per, "tokens": T, "topk": k}
 
 
-def bench_w4a4(torch, q4, workloads, dev, seed):
-    log("generating the W4A4 workload (8192^3)")
+def bench_w4a4(torch, q4, workloads, dev, seed, fmt="mxfp4"):
+    """W4A4 GEMM 8192^3, both operands in `fmt`: MXFP4 on the block-scaled
+    FP4 matrix cores (fraction of the FP4 peak), NVFP4 on the fp16 matrix
+    cores with both operands dequantized exactly (fraction of the fp16
+    peak); plus the activation quantize (NVFP4: tensor amax pass included)."""
+    log(f"generating the W4A4 workload (8192^3, {fmt})")
     wl = workloads.w4a4_gemm(seed=seed)
     A = wl.tensors["A"].to(dev)
     W = wl.tensors["W"].to(dev)
     M, K = A.shape
     N = W.shape[0]
-    qw = q4.quantize(W, "mxfp4", layout="tiled")
-    qa = q4.quantize(A, "mxfp4", layout="tiled")
+    qw = q4.quantize(W, fmt, layout="tiled")
+    qa = q4.quantize(A, fmt, layout="tiled")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     ms = timed(torch, lambda: q4.q4_gemm(qa, qw, C), 10, 2)
     ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    peak = ("frac_fp4_peak", FP4_PEAK_TFLOPS) if fmt == "mxfp4" else ("frac_fp16_peak", FP16_PEAK_TFLOPS)
     return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
-            "frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+            peak[0]: round(tflops / peak[1], 4),
             "act_quantize_us": round(ams * 1e3, 1),
             "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
 

@@ -200,6 +200,17 @@ q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx
  *   A_q (MXFP4, rows M, cols K) with W MXFP4 -> W4A4: both operands enter
  *                       the block-scaled FP4 matrix cores directly (same
  *                       table, row W4A4);
+ *   A_q (NVFP4, rows M, cols K) with W NVFP4 -> W4A4 NVFP4: each code times
+ *                       its E4M3 block scale is exact in fp16, so both
+ *                       operands are dequantized to fp16 in registers and
+ *                       multiplied on fp16 matrix cores; the two tensor
+ *                       scales are applied to the fp32 sum:
+ *                       C = (sum_k (qa sa)(qw sw)) * gs_a * gs_w.  A_q's
+ *                       global_scale is its own (q4_quantize of A computes
+ *                       it from A's amax, or takes the caller's).  gfx950's
+ *                       FP4 matrix cores take E8M0 scales per 32, which
+ *                       cannot carry E4M3 per 16 ("Quantization in
+ *                       deployment", cheat sheet, NVFP4 and MXFP4 rows);
  *   A_q (Q4_FP8_ROW, rows M, cols K) with W INT4 -> W4A8: the INT4 codes
  *                       become exact E4M3 values, the products run on FP8
  *                       matrix cores, and each 128-wide group's partial sum

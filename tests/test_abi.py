@@ -131,6 +131,16 @@ def test_gemm_validation():
     assert L.q4_gemm(64, A16, 512, ctypes.byref(a), ctypes.byref(w), A16, 512, None) == FMT
     assert L.q4_gemm(64, None, 512, None, ctypes.byref(w), A16, 512, None) == NULL
     assert L.q4_gemm(64, None, 0, ctypes.byref(nv), ctypes.byref(w), A16, 512, None) == FMT
+    # W4A4 takes both operands in one FP4 format: NVFP4 x NVFP4 is accepted
+    nvw = desc(fmt=q4.NVFP4, rows=512, cols=512, gs=A16)
+    assert L.q4_gemm(64, None, 0, ctypes.byref(a), ctypes.byref(nvw), A16, 512, None) == FMT
+    assert L.q4_gemm(64, None, 0, ctypes.byref(nv), ctypes.byref(desc(fmt=q4.INT4_G128, rows=512, cols=512)),
+                     A16, 512, None) == FMT
+    assert L.q4_gemm(32, None, 0, ctypes.byref(nv), ctypes.byref(nvw), A16, 512, None) == SHAPE
+    assert L.q4_gemm(64, None, 0, ctypes.byref(nv), ctypes.byref(desc(fmt=q4.NVFP4, rows=512, cols=512)),
+                     A16, 512, None) == NULL                      # an NVFP4 weight needs its global scale
+    assert L.q4_gemm(0, None, 0, ctypes.byref(desc(fmt=q4.NVFP4, rows=0, cols=512, gs=A16)),
+                     ctypes.byref(nvw), A16, 512, None) == OK
     assert L.q4_gemm(32, None, 0, ctypes.byref(a), ctypes.byref(w), A16, 512, None) == SHAPE
     assert L.q4_gemm(64, A16, 512, None, ctypes.byref(desc(rows=512, cols=96)), A16, 512,
                      None) == SHAPE

@@ -301,6 +301,81 @@ def test_full_w4a4_gemm():
 
 
 # --------------------------------------------------------------------------
+# W4A4 NVFP4 GEMM (both operands NVFP4, each with its own global scale)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("alayout,wlayout", [("rows", "rows"), ("tiled", "tiled"),
+                                             ("rows", "tiled"), ("tiled", "rows")])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (129, 1000, 1024), (65, 1030, 2048),
+                                   (300, 520, 1536)])
+def test_gemm_w4a4_nvfp4_small(M, N, K, alayout, wlayout):
+    if "tiled" in (alayout, wlayout) and not tiled_ok(K):
+        pytest.skip("the tiled layout needs K % 512 == 0")
+    log("gemm w4a4 nvfp4", alayout, wlayout, M, N, K)
+    w = workloads.matrix(f"t4n/w{N}x{K}", N, K, 0.02, seed=45, outlier_frac=0.001, outlier_mult=20.0)
+    a = workloads.matrix(f"t4n/a{M}x{K}", M, K, 1.0, seed=46, channel_frac=0.01, channel_mult=10.0)
+    qw, qwr = quantized(w, "nvfp4", wlayout)
+    qa, qar = quantized(a, "nvfp4", alayout)
+    C = torch.full((M, N + 4), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q4.q4_gemm(qa, qw, C[:, :N])
+    torch.cuda.synchronize()
+    Cc = C.cpu()
+    assert torch.isnan(Cc[:, N:]).all()
+    ad, wd = oracle.dequant(qar), oracle.dequant(qwr)
+    check_matmul(Cc[:, :N], oracle.gemm_w4a4(None, qwr, aq=qar), ad, wd, True, "w4a4 nvfp4")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_w4a4_nvfp4_identity_a_returns_w_transposed(layout):
+    """NVFP4 maps A = I exactly, so C = w'^T within the output rounding."""
+    K = 512
+    w = tiny_rows(128, K, 47)          # scales spanning six decades, E4M3 subnormals included
+    qw, qwr = quantized(w, "nvfp4", layout)
+    qa, qar = quantized(torch.eye(K, dtype=torch.bfloat16), "nvfp4", layout)
+    assert np.array_equal(oracle.dequant(qar), np.eye(K, dtype=np.float32))
+    C = torch.empty((K, 128), dtype=torch.bfloat16, device=DEV)
+    q4.q4_gemm(qa, qw, C)
+    torch.cuda.synchronize()
+    wd = oracle.dequant(qwr)
+    check_matmul(C.cpu(), wd.T.astype(np.float64), np.eye(K, dtype=np.float32), wd, True, "w4a4 nvfp4 I")
+
+
+def test_w4a4_nvfp4_power_of_two_scaling_of_a():
+    """A -> 4A leaves every code and block scale and moves A's global scale
+    by 4, so C -> 4C exactly (the global scales enter after the sum)."""
+    M, N, K = 128, 256, 1024
+    w = workloads.matrix("t4n/pw", N, K, 0.02, seed=48)
+    a = workloads.matrix("t4n/pa", M, K, 1.0, seed=49)
+    qw, _ = quantized(w, "nvfp4", "tiled")
+    out = []
+    for f in (1.0, 4.0):
+        qa = q4.quantize((a.float() * f).to(torch.bfloat16).to(DEV), "nvfp4", layout="tiled")
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemm(qa, qw, C)
+        out.append(C.float().cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(out[1], out[0] * 4.0)
+
+
+def test_full_w4a4_nvfp4_gemm():
+    """8192^3 W4A4 with NVFP4 operands (the W4A4 workload's A and W): 64
+    sampled rows of C against the oracle (A's global scale from the whole A)."""
+    wl = workloads.w4a4_gemm()
+    A, W = wl.tensors["A"], wl.tensors["W"]
+    M, N = A.shape[0], W.shape[0]
+    log("w4a4 nvfp4: quantize (tiled)")
+    qw, qwr = quantized(W, "nvfp4", "tiled")
+    qa, qar = quantized(A, "nvfp4", "tiled")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    q4.q4_gemm(qa, qw, C)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(50).choice(M, 62, replace=False)]))
+    ref = oracle.gemm_w4a4(None, qwr, rows=rows, aq=qar)
+    ad = oracle.dequant_rows(qar, rows)
+    e = check_matmul(C.cpu()[torch.from_numpy(rows)], ref, ad, oracle.dequant(qwr), True, "w4a4 nvfp4 8192")
+    log("w4a4 nvfp4 max normalized error", e)
+
+
+# --------------------------------------------------------------------------
 # grouped MoE GEMM
 # --------------------------------------------------------------------------
 def _grouped_case(E, N, K, T, topk, seed, fmt="mxfp4"):

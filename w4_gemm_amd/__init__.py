@@ -241,8 +241,9 @@ def q4_gemv(W: Q4Tensor, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch
 
 
 def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
-    """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16), an MXFP4 Q4Tensor
-    (W4A4, with W MXFP4) or an FP8_ROW Q4Tensor (W4A8, with W INT4)."""
+    """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16), an MXFP4 or NVFP4
+    Q4Tensor (W4A4, with W in the same format) or an FP8_ROW Q4Tensor (W4A8,
+    with W INT4)."""
     wd = W.c()
     if isinstance(A, Q4Tensor):
         ad = A.c()

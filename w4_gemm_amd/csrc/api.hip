@@ -80,7 +80,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 extern "C" {
 
-int q4_version(void) { return 101; }
+int q4_version(void) { return 102; }
 
 const char* q4_status_string(int status) {
   switch (status) {
@@ -183,7 +183,7 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
   if (A_q) {
     st = check_tensor(A_q);
     if (st != Q4_OK) return st;
-    const bool w4a4 = A_q->fmt == Q4_MXFP4 && W->fmt == Q4_MXFP4;
+    const bool w4a4 = A_q->fmt == W->fmt && (W->fmt == Q4_MXFP4 || W->fmt == Q4_NVFP4);
     const bool w4a8 = A_q->fmt == Q4_FP8_ROW && W->fmt == Q4_INT4_G128;
     if (!w4a4 && !w4a8) return Q4_ERR_FORMAT;
     if (A_q->rows != M || A_q->cols != K) return Q4_ERR_SHAPE;
@@ -201,6 +201,11 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
         A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const float*>(A_q->scales),
         M, static_cast<const uint8_t*>(W->codes), static_cast<const uint16_t*>(W->scales), N, K,
         static_cast<uint16_t*>(C_bf16), ldc, as_stream(stream)));
+  if (A_q && A_q->fmt == Q4_NVFP4)
+    return hip_status(q4::launch_gemm_w4a4_nvfp4(
+        A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales),
+        A_q->global_scale, M, static_cast<const uint8_t*>(W->codes), static_cast<const uint8_t*>(W->scales),
+        W->global_scale, N, K, static_cast<uint16_t*>(C_bf16), ldc, as_stream(stream)));
   if (A_q)
     return hip_status(q4::launch_gemm_w4a4(
         A_q->layout, W->layout, static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,

@@ -48,6 +48,14 @@ hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scale
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
 
+// W4A4 NVFP4 GEMM C [M][ldc] = A' . W'^T, both NVFP4 (E4M3 per 16, each
+// operand's fp32 tensor scale a_gs / w_gs on the device), K % 128 == 0:
+// fp16 matrix cores on exactly dequantized operands (gemm_w4a4_nv.hip).
+hipError_t launch_gemm_w4a4_nvfp4(int a_layout, int w_layout, const uint8_t* a_codes, const uint8_t* a_scales,
+                                  const float* a_gs, int64_t M, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, const float* w_gs, int64_t N, int64_t K,
+                                  uint16_t* C, int64_t ldc, hipStream_t stream);
+
 // Per-token FP8 (E4M3) quantization of bf16 src [rows][ld] into codes
 // (row-major [rows][cols] or the tiled FP8 layout) and fp32 scales [rows].
 hipError_t launch_fp8_rows_quantize(int layout, const uint16_t* src, int64_t ld, int64_t rows,
