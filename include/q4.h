@@ -93,6 +93,9 @@
  *     calling thread's last failure.
  *   - Inputs must be finite.  Calls on distinct outputs may run
  *     concurrently; outputs must not alias inputs.
+ *   - The first launch of a kernel that uses more than 64 KB of LDS on a
+ *     device raises that kernel's LDS limit there (hipFuncSetAttribute, once
+ *     per kernel and device); no other state is kept.
  */
 #ifndef Q4_H
 #define Q4_H

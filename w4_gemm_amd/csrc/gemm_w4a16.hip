@@ -265,9 +265,7 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
 template <int FMT>
 hipError_t run(const uint16_t* A, int64_t lda, int64_t M, const uint8_t* codes, const void* scales,
                const float* gs, int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w4a16_tiled_kernel<FMT>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kSmemBytes);
+  const hipError_t attr = set_max_lds<&w4a16_tiled_kernel<FMT>>(kSmemBytes);
   if (attr != hipSuccess) return attr;
   const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
   w4a16_tiled_kernel<FMT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(

@@ -223,9 +223,7 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
 hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&w4a4_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kSmemBytes);
+  const hipError_t attr = set_max_lds<&w4a4_tiled_kernel>(kSmemBytes);
   if (attr != hipSuccess) return attr;
   const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
   w4a4_tiled_kernel<<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(a_codes, a_scales, (int)M, w_codes,

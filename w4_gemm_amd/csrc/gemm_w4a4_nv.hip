@@ -296,8 +296,7 @@ hipError_t run_tiled(const uint8_t* a_codes, const uint8_t* a_scales, const floa
                      uint16_t* C, int64_t ldc, hipStream_t stream) {
   using Sh = NvShape<WM, WN, TM, TN>;
   auto* kern = &w4a4nv_tiled_kernel<WM, WN, TM, TN>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::kSmem);
+  const hipError_t attr = set_max_lds<&w4a4nv_tiled_kernel<WM, WN, TM, TN>>(Sh::kSmem);
   if (attr != hipSuccess) return attr;
   const int64_t BR = Sh::kBMT * 16, BC = Sh::kBNT * 16;
   const int64_t T = ((M + BR - 1) / BR) * ((N + BC - 1) / BC);

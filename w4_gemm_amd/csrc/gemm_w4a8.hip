@@ -323,9 +323,7 @@ hipError_t launch_gemm_w4a8(int a_layout, int w_layout, const uint8_t* a_codes, 
                             int64_t M, const uint8_t* w_codes, const uint16_t* w_scales, int64_t N,
                             int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
   if (a_layout == kLayoutTiled && w_layout == kLayoutTiled) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&w4a8_tiled_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)kSmemBytes);
+    const hipError_t attr = set_max_lds<&w4a8_tiled_kernel>(kSmemBytes);
     if (attr != hipSuccess) return attr;
     const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
     w4a8_tiled_kernel<<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(

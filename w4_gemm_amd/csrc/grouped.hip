@@ -323,9 +323,7 @@ template <int FMT, bool SWIGLU>
 hipError_t run(const uint16_t* A, int64_t lda, int64_t T, const int32_t* gather, const int32_t* offsets,
                int32_t E, int64_t P, const uint8_t* codes, const void* scales, const float* gs,
                int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&grouped_tiled_kernel<FMT, SWIGLU>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kSmemBytes);
+  const hipError_t attr = set_max_lds<&grouped_tiled_kernel<FMT, SWIGLU>>(kSmemBytes);
   if (attr != hipSuccess) return attr;
   const int64_t NT = N / 16;
   const dim3 grid((unsigned)((NT + kWaves * kTPW - 1) / (kWaves * kTPW)), (unsigned)E);

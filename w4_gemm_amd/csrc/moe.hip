@@ -195,9 +195,7 @@ hipError_t launch_moe_route(const float* logits, int64_t ld, int64_t T, int32_t 
     moe_topk_kernel<<<grid, 64 * kRouteWaves, 0, stream>>>(logits, ld, (int)T, E, k, ids, weights);
   }
   const size_t lds = moe_dispatch_lds_bytes(T, E);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&moe_dispatch_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)kMoeDispatchMaxLds);
+  const hipError_t attr = set_max_lds<&moe_dispatch_kernel>(kMoeDispatchMaxLds);
   if (attr != hipSuccess) return attr;
   moe_dispatch_kernel<<<1, kDispatchThreads, lds, stream>>>(ids, (int)T, E, k, offsets, gather, inv);
   return hipGetLastError();

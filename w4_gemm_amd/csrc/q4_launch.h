@@ -6,7 +6,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace q4 {
+
+// Raises KERNEL's dynamic LDS limit to `bytes` on the current device, once
+// per device (the attribute belongs to the kernel on that device; devices
+// 0..63 are remembered, others set it on every call).
+template <auto KERNEL>
+hipError_t set_max_lds(size_t bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERNEL), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // Quantize bf16 src [rows][ld] into codes/scales (fmt 0 INT4 g128,
 // 1 MXFP4, 2 NVFP4; layout 0 row-major, 1 tiled).  NVFP4: gs receives the
