@@ -39,6 +39,7 @@
 //     4 consecutive columns of one row of C: 8-byte stores.
 #include "q4_launch.h"
 #include "q4_layout.h"
+#include "q4_lds.h"
 #include "q4_mma.h"
 
 #include <type_traits>
@@ -52,30 +53,6 @@ constexpr int kColTiles = 4 * kWaves;           // 16-column weight tiles per bl
 constexpr int kAFrags = 2 * kRowTiles;          // activation fragments per stage
 constexpr int kABufs = 3;
 constexpr size_t kSmemBytes = kABufs * kAFrags * 1024 + 2 * kColTiles * 1024;  // 112 KB
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint8_t* lds_base) {
-  // each lane copies 16 bytes from src to lds_base + 16 * lane
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
-}
-
-// Barrier that does not wait for outstanding copies (each wave has waited
-// for its own by count before it); nothing may be moved across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
 
 // Loads issued for running stage v (group v): the stage's activation
 // fragments (2 per wave), the weight tiles of super-chunk v/2 when v is

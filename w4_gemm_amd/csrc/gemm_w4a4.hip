@@ -32,6 +32,7 @@
 //     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
 #include "q4_launch.h"
 #include "q4_layout.h"
+#include "q4_lds.h"
 #include "q4_mma.h"
 
 namespace q4 {
@@ -44,31 +45,6 @@ constexpr int kWaves = 8;
 constexpr int kCopies = kTiles / kWaves;  // code tiles each wave copies per stage
 constexpr int kCodeBufs = 3;
 constexpr size_t kSmemBytes = kCodeBufs * kTiles * 1024 + 2 * kTiles * 256;  // 112 KB
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  // each lane copies 16 bytes from src to lds_base + 16 * lane
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base,
-                                   16, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier that orders LDS accesses without waiting for the
-// outstanding global->LDS copies (the wave's own copies are waited for
-// explicitly, by count, before it).  The empty asm statements keep the
-// compiler from moving memory accesses across the barrier.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 __global__ void __launch_bounds__(kWaves * 64)
 w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -180,23 +156,23 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
   for (int s0 = 0; s0 < S; s0 += 4) {
     // j = 0
     wait_vmcnt<kCopies>();
-    stage_barrier();
+    stage_barrier_loose();
     issue_codes(s0 + 2);
     compute(s0, 0);
     // j = 1
     wait_vmcnt<kCopies>();
-    stage_barrier();
+    stage_barrier_loose();
     issue_codes(s0 + 3);
     compute(s0 + 1, 1);
     // j = 2: group s0+4 starts a new scale group
     wait_vmcnt<kCopies>();
-    stage_barrier();
+    stage_barrier_loose();
     issue_codes(s0 + 4);
     issue_scales(s0 + 4);
     compute(s0 + 2, 2);
     // j = 3: group s0+4 (outstanding) also holds its scale copy
     wait_vmcnt<kCopies + 1>();
-    stage_barrier();
+    stage_barrier_loose();
     issue_codes(s0 + 5);
     compute(s0 + 3, 3);
   }

@@ -45,6 +45,7 @@
 // k; those eight codes lie in the lane's 16-block i/2.
 #include "q4_launch.h"
 #include "q4_layout.h"
+#include "q4_lds.h"
 #include "q4_mma.h"
 
 namespace q4 {
@@ -106,33 +107,6 @@ struct NvShape {
   static_assert(kTiles % kWaves == 0, "code copies per wave");
   static_assert(kSmem <= 160 * 1024, "LDS");
 };
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-// each lane copies 16 (4) bytes from src to lds_base + 16 (4) * lane
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void copy4_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier ordering LDS accesses, without waiting for the
-// outstanding global->LDS copies (each wave waits for its own, by count).
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
 
 template <int WM, int WN, int TM, int TN>
 __global__ void __launch_bounds__(WM * WN * 64)

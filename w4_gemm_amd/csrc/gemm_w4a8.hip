@@ -31,6 +31,7 @@
 // order, for the shapes and layouts the tiled kernel does not take.
 #include "q4_launch.h"
 #include "q4_layout.h"
+#include "q4_lds.h"
 #include "q4_mma.h"
 
 namespace q4 {
@@ -85,39 +86,6 @@ constexpr int kSBytes = kBN * 128;  // fp16 W scales of one group of four stages
 constexpr int kCopies = (kBM * kABytes + kBN * kWBytes) / 1024 / kWaves;  // 1 KB copies per wave per stage
 constexpr size_t kSmemBytes = (size_t)kBufs * (kBM * kABytes + kBN * kWBytes) + 2 * kSBytes;  // 148 KB
 static_assert(kCopies == 6, "copy plan");
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void copy4_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
-}
-
-// A wave-uniform pointer held in scalar registers (readfirstlane), so that
-// adding the lane offset at each copy cannot be hoisted into per-lane
-// 64-bit registers for the whole loop.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
 
 __global__ void __launch_bounds__(kWaves * 64)
 w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__ a_scales, int M,

@@ -40,6 +40,7 @@
 //     output row written as zeros.
 #include "q4_launch.h"
 #include "q4_layout.h"
+#include "q4_lds.h"
 #include "q4_mma.h"
 
 namespace q4 {
@@ -56,33 +57,6 @@ constexpr int kXThreads = kRows * 16 / 2;  // threads staging activations, 2 pie
 constexpr size_t kWBytes = (size_t)kWBufs * kTiles * 1024;               // 48 KB
 constexpr size_t kSmemBytes = kWBytes + 2ull * kRows * kXRow * 2;        // + 25.5 KB
 static_assert(kXThreads % 64 == 0 && kXThreads <= kWaves * 64, "staging split");
-
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
-
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-}
 
 // raw scale words of one weight tile for one group of four super-chunks
 template <int FMT>
