@@ -186,6 +186,45 @@ def test_full_mxfp4_decode_gemv(layout):
         log("mxfp4 decode gemv B", B, "max normalized error", e)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_strided_operands_match_contiguous(fmt, layout):
+    """Row strides of x / A and of y / C larger than the rows (column slices
+    of wider tensors) give bit for bit the contiguous results: GEMV, W4A16
+    GEMM and the grouped GEMM."""
+    N, K = 272, 1024
+    w = workloads.matrix("tst/w", 4 * N, K, 0.02, seed=61)
+    qg, _ = quantized(w, fmt, layout)
+    qn, _ = quantized(w[:N], fmt, layout)
+    a = workloads.matrix("tst/a", 40, K, 1.0, seed=62).to(DEV)
+    wide = torch.full((40, K + 64), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide[:, :K] = a
+    a_s = wide[:, :K]
+    for B in (1, 16):
+        y0 = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+        y1 = torch.full((B, N + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemv(qn, a[:B].contiguous(), y0)
+        q4.q4_gemv(qn, a_s[:B], y1[:, :N])
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1[:, :N]) and torch.isnan(y1[:, N:]).all()
+    c0 = torch.empty((40, N), dtype=torch.bfloat16, device=DEV)
+    c1 = torch.full((40, N + 24), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q4.q4_gemm(a, qn, c0)
+    q4.q4_gemm(a_s, qn, c1[:, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1[:, :N]) and torch.isnan(c1[:, N:]).all()
+    logits = workloads.normal_f32("tst/l", 40 * 4, seed=63).reshape(40, 4)
+    r = workloads.route(logits, 2)
+    ga, of = torch.from_numpy(r.gather).to(DEV), torch.from_numpy(r.offsets).to(DEV)
+    P = len(r.gather)
+    g0 = torch.empty((P, N), dtype=torch.bfloat16, device=DEV)
+    g1 = torch.full((P, N + 8), float("nan"), dtype=torch.bfloat16, device=DEV)
+    q4.q4_grouped_gemm(a, ga, of, qg, N, g0)
+    q4.q4_grouped_gemm(a_s, ga, of, qg, N, g1[:, :N])
+    torch.cuda.synchronize()
+    assert torch.equal(g0, g1[:, :N]) and torch.isnan(g1[:, N:]).all()
+
+
 # --------------------------------------------------------------------------
 # W4A16 GEMM
 # --------------------------------------------------------------------------
