@@ -34,6 +34,7 @@ FP16_PEAK_TFLOPS = 2500.0      # dense fp16 matrix cores (the W4A4 NVFP4 kernel'
 FP4_PEAK_TFLOPS = 10100.0      # dense MXFP4 matrix cores
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 matrix cores
 GRAPH_STEPS = 10               # decode steps captured per HIP graph in the timed loop
+IDLE_GAP_S = 0.5               # idle time before each extra workload
 METRIC = "W4 GEMV weight GB/s and W4 GEMM TFLOP/s vs MI355X roofline, 1 GPU"
 
 
@@ -274,20 +275,25 @@ def main():
     def want(name):
         return not args.no_extra and (not only or name in only)
 
-    if want("int4"):
-        extra["int4_g128_gemv_1024"] = bench_int4(torch, q4, workloads, dev, args.seed)
-    if want("nvfp4"):
-        extra["nvfp4_w4a16_gemm_4096x8192x8192"] = bench_nvfp4(torch, q4, workloads, dev, args.seed)
-    if want("moe"):
-        extra["moe_grouped_mxfp4_64x2048x7168"] = bench_moe(torch, q4, workloads, dev, args.seed)
-    if want("w4a4"):
-        extra["w4a4_mxfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed)
-    if want("w4a4_nvfp4"):
-        extra["w4a4_nvfp4_gemm_8192"] = bench_w4a4(torch, q4, workloads, dev, args.seed, "nvfp4")
-    if want("moe_layer"):
-        extra["moe_layer_mxfp4_64x(2x2048|7168)"] = bench_moe_layer(torch, q4, workloads, dev, args.seed)
-    if want("w4a8"):
-        extra["w4a8_int4_fp8_gemm_4096x8192x8192"] = bench_w4a8(torch, q4, workloads, dev, args.seed)
+    # HBM-bound workloads first, then the matrix-core-bound ones, each after
+    # a short idle gap, so that no measurement inherits the power state (and
+    # lower clock) of a long compute-bound run before it
+    runs = [
+        ("int4", "int4_g128_gemv_1024", lambda: bench_int4(torch, q4, workloads, dev, args.seed)),
+        ("moe", "moe_grouped_mxfp4_64x2048x7168", lambda: bench_moe(torch, q4, workloads, dev, args.seed)),
+        ("moe_layer", "moe_layer_mxfp4_64x(2x2048|7168)",
+         lambda: bench_moe_layer(torch, q4, workloads, dev, args.seed)),
+        ("nvfp4", "nvfp4_w4a16_gemm_4096x8192x8192", lambda: bench_nvfp4(torch, q4, workloads, dev, args.seed)),
+        ("w4a4", "w4a4_mxfp4_gemm_8192", lambda: bench_w4a4(torch, q4, workloads, dev, args.seed)),
+        ("w4a8", "w4a8_int4_fp8_gemm_4096x8192x8192", lambda: bench_w4a8(torch, q4, workloads, dev, args.seed)),
+        ("w4a4_nvfp4", "w4a4_nvfp4_gemm_8192",
+         lambda: bench_w4a4(torch, q4, workloads, dev, args.seed, "nvfp4")),
+    ]
+    for name, key, fn in runs:
+        if want(name):
+            torch.cuda.synchronize()
+            time.sleep(IDLE_GAP_S)
+            extra[key] = fn()
 
     cpu = None
     if not args.no_cpu_baseline:
