@@ -218,8 +218,10 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
     store_x(0);
     auto iteration = [&](int st, auto jc) {
       constexpr int J = decltype(jc)::value;
-      if constexpr (J == 3) wait_vmcnt<kTPW + kSLoads>();
-      else wait_vmcnt<kTPW>();
+      // this wave's weight copies of stage st and its x(st) writes to LDS
+      // complete, then the barrier makes every wave's visible
+      if constexpr (J == 3) wait_vmcnt_lgkm0<kTPW + kSLoads>();
+      else wait_vmcnt_lgkm0<kTPW>();
       stage_barrier();
       if constexpr (J == 0) {
 #pragma unroll
