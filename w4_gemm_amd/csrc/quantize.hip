@@ -499,7 +499,9 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
       set_word_kernel<<<1, 1, 0, stream>>>(amax, 0u);
       if (chunks) {
         if (rows > 0 && cols > 0) {
-          const unsigned agrid = (unsigned)(rows < 2048 ? rows : 2048);
+          // one workgroup per CU: with 2048 workgroups the final atomic max
+          // of each one serialized into a tail (8192^2 NVFP4: 82 -> 69 us)
+          const unsigned agrid = (unsigned)(rows < 256 ? rows : 256);
           absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
         }
         launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, 1, nullptr, stream);
