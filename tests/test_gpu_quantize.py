@@ -111,6 +111,32 @@ def test_quantize_exact_ties(fmt):
     assert_quant_equal(qg, qr, fmt)
 
 
+@pytest.mark.parametrize("cols", (128, 48))
+def test_nvfp4_quotients_next_to_rounding_boundaries(cols):
+    """NVFP4 quotients a few ulp either side of every E2M1 rounding boundary.
+    With the caller's tensor scale gs = 1 + k 2^-23 and a block whose absmax
+    is 6v (v an E4M3 value), the block scale is v and w = b v divides to
+    b / gs: within |k| ulp of the boundary b.  The code is the rounding of
+    the fp32 quotient, so this is where a shortcut around the division would
+    have to be exact.  cols 128 takes the block-mapped kernel, 48 the
+    per-chunk one."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    vs = np.array([m / 8.0 * 2.0 ** e for e in range(-6, 8) for m in range(8, 16)], np.float32)
+    blocks = np.zeros((vs.size, 16), np.float32)
+    blocks[:, 0] = 6.0 * vs
+    blocks[:, 1:8] = mids[None, :] * vs[:, None]
+    blocks[:, 8:15] = -mids[None, :] * vs[:, None]
+    per_row = cols // 16
+    n = (blocks.shape[0] // per_row) * per_row
+    w = torch.from_numpy(blocks[:n].reshape(-1, cols)).to(torch.bfloat16)
+    assert np.array_equal(to_f32(w).reshape(-1, 16), blocks[:n])  # every value exact in bf16
+    for k in (-40, -12, -6, -3, -2, -1, 0, 1, 2, 3, 6, 12, 40):
+        gs = float(np.float32(1.0 + k * 2.0 ** -23))
+        log("nvfp4 near boundaries", cols, k)
+        qg, qr = quant_both(w, "nvfp4", gs=gs)
+        assert_quant_equal(qg, qr, "nvfp4")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
 def test_quantize_edge_blocks(fmt, layout):

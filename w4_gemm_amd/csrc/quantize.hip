@@ -66,6 +66,56 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const Chunk8& c, float scale) {
   return p;
 }
 
+// The divisions of NVFP4 (w / eff for every value, (amax / 6) / gs for
+// every block scale) are fp32 divisions, correctly rounded, whose results
+// are then rounded to a short format (E2M1, E4M3) by a rounding that is
+// monotone in the value.  Each is done here as a product with reciprocals,
+// twice, with the product nudged down and up by a relative 2^-20: the
+// reciprocals (v_rcp_f32, within 1 ulp; an fp32 division, within 1/2 ulp)
+// and the products add under 2^-21 relative error in all, so the two
+// nudged products bracket the correctly rounded quotient.  Where both round
+// to the same code, so does the quotient; where they differ (a quotient
+// within about 2^-20 of a rounding boundary, an exact tie) the division is
+// done.  This needs every operand in the normal range: the callers take
+// this path only for scales within [2^-100, 2^100]; a product that
+// overflows stands for a quotient that rounds to the top code on both
+// sides, one that underflows for a quotient whose code magnitude is 0.
+constexpr float kNudgeDown = 1.0f - 0x1p-20f, kNudgeUp = 1.0f + 0x1p-20f;
+
+__device__ __forceinline__ bool nv_in_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+
+// E2M1 codes of x[j] / eff.
+__device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
+  if (nv_in_range(eff)) {
+    const float r = __builtin_amdgcn_rcpf(eff);
+    const float rl = r * kNudgeDown, rh = r * kNudgeUp;
+    Chunk8 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo.v[j] = x.v[j] * rl;
+      hi.v[j] = x.v[j] * rh;
+    }
+    const uint32_t pl = e2m1_pack8(lo, 1.0f), ph = e2m1_pack8(hi, 1.0f);
+    if (__builtin_expect(pl == ph, 1)) return pl;
+  }
+  Chunk8 y;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y.v[j] = x.v[j] / eff;  // fp32 division by the scale as used
+  return e2m1_pack8(y, 1.0f);
+}
+
+// E4M3 code of min((amax / 6) / gs, 448); rgs = 1 / gs (an fp32 division),
+// gs_ok = nv_in_range(gs).
+__device__ __forceinline__ uint32_t nv_scale_code(float amax, float gs, float rgs, bool gs_ok) {
+  if (gs_ok) {
+    const float a = amax * rgs;
+    const uint32_t cl = e4m3_encode(fminf(a * (kNudgeDown / 6.0f), 448.0f));
+    const uint32_t ch = e4m3_encode(fminf(a * (kNudgeUp / 6.0f), 448.0f));
+    if (__builtin_expect(cl == ch, 1)) return cl;
+  }
+  return e4m3_encode(fminf((amax / 6.0f) / gs, 448.0f));
+}
+
 template <int LANES>
 __device__ __forceinline__ float group_max(float a) {
 #pragma unroll
@@ -150,6 +200,8 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
       if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
     }
   }
+  const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
+  const bool gs_ok = FMT == 2 && nv_in_range(gs);
 
   for (int64_t base = (int64_t)blockIdx.x * kThreads; base < total;
        base += (int64_t)gridDim.x * kThreads) {
@@ -188,17 +240,13 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
       if (valid && (k0 % G) == 0)
         reinterpret_cast<uint8_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint8_t)e;
     } else {
-      const float t = fminf((amax / 6.0f) / gs, 448.0f);
-      const uint32_t sc = e4m3_encode(t);
+      const uint32_t sc = nv_scale_code(amax, gs, rgs, gs_ok);
       const float eff = e4m3_value(sc) * gs;
       if (eff == 0.0f) {  // E4M3 scale underflowed to 0: magnitude codes 0, signs kept
 #pragma unroll
         for (int j = 0; j < 8; ++j) packed |= ((f2u(x.v[j]) >> 31) << 3) << (4 * j);
       } else {
-        Chunk8 y;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) y.v[j] = x.v[j] / eff;  // fp32 division by the scale as used
-        packed = e2m1_pack8(y, 1.0f);
+        packed = e2m1_pack8_div(x, eff);
       }
       if (valid && (k0 % G) == 0)
         reinterpret_cast<uint8_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint8_t)sc;
@@ -236,6 +284,8 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
       if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
     }
   }
+  const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
+  const bool gs_ok = FMT == 2 && nv_in_range(gs);
 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -321,8 +371,7 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float amax = fmaxf(absmax8(x[2 * h]), absmax8(x[2 * h + 1]));
-      const float t = fminf((amax / 6.0f) / gs, 448.0f);
-      const uint32_t sc = e4m3_encode(t);
+      const uint32_t sc = nv_scale_code(amax, gs, rgs, gs_ok);
       const float eff = e4m3_value(sc) * gs;
       sc2[h] = sc;
 #pragma unroll
@@ -333,10 +382,7 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
           for (int j = 0; j < 8; ++j) p |= ((f2u(x[i].v[j]) >> 31) << 3) << (4 * j);
           packed[i] = p;
         } else {
-          Chunk8 y;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y.v[j] = x[i].v[j] / eff;  // fp32 division by the scale as used
-          packed[i] = e2m1_pack8(y, 1.0f);
+          packed[i] = e2m1_pack8_div(x[i], eff);
         }
       }
     }
