@@ -111,6 +111,34 @@ def test_quantize_exact_ties(fmt):
     assert_quant_equal(qg, qr, fmt)
 
 
+@pytest.mark.parametrize("fmt", ("int4", "int4_zp"))
+@pytest.mark.parametrize("layout", ("rows", "tiled"))
+def test_int4_exact_ties(fmt, layout):
+    """Half-integer quotients as exact ties: -6.5 .. 6.5 (INT4), -7.5 .. 6.5
+    and, with a zero point of -4, -3.5 .. 10.5 (INT4 with zero point).  Each
+    group's scale is a power of two (INT4: absmax 7 2^e; zero point: range
+    [lo, hi] with (hi - lo) / 15 = 2^e), and the values are (k + 1/2) 2^e."""
+    rows = []
+    for e in range(-10, 10):
+        for lo_k, hi_k in ((-8, 7), (-4, 11)):
+            if fmt == "int4" and lo_k != -8:
+                continue
+            ks = np.arange(-7 if fmt == "int4" else lo_k, 7 if fmt == "int4" else hi_k, dtype=np.float32)
+            ties = (ks + 0.5) * np.float32(2.0 ** e)
+            g = np.resize(np.concatenate([ties, -ties if fmt == "int4" else ties]), 128).astype(np.float32)
+            if fmt == "int4":
+                g[0] = 7.0 * 2.0 ** e      # absmax -> s = fp16(7 2^e / 7) = 2^e
+            else:
+                g[0], g[1] = lo_k * 2.0 ** e, hi_k * 2.0 ** e
+            rows.append(np.concatenate([g, g[::-1], g[::-1], g]))  # 512: a tiled row
+    x = np.stack(rows)
+    w = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(to_f32(w), x)
+    log("int4 ties", fmt, layout, tuple(w.shape))
+    qg, qr = quant_both(w, fmt, layout=layout)
+    assert_quant_equal(qg, qr, fmt)
+
+
 @pytest.mark.parametrize("cols", (128, 48))
 def test_nvfp4_quotients_next_to_rounding_boundaries(cols):
     """NVFP4 quotients a few ulp either side of every E2M1 rounding boundary.

@@ -66,27 +66,27 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const Chunk8& c, float scale) {
   return p;
 }
 
-// The divisions of NVFP4 (w / eff for every value, (amax / 6) / gs for
-// every block scale) are fp32 divisions, correctly rounded, whose results
-// are then rounded to a short format (E2M1, E4M3) by a rounding that is
-// monotone in the value.  Each is done here as a product with reciprocals,
-// twice, with the product nudged down and up by a relative 2^-20: the
-// reciprocals (v_rcp_f32, within 1 ulp; an fp32 division, within 1/2 ulp)
-// and the products add under 2^-21 relative error in all, so the two
-// nudged products bracket the correctly rounded quotient.  Where both round
-// to the same code, so does the quotient; where they differ (a quotient
-// within about 2^-20 of a rounding boundary, an exact tie) the division is
-// done.  This needs every operand in the normal range: the callers take
-// this path only for scales within [2^-100, 2^100]; a product that
-// overflows stands for a quotient that rounds to the top code on both
-// sides, one that underflows for a quotient whose code magnitude is 0.
+// Division by a block scale.  Each code is a correctly rounded fp32
+// quotient w / s (NVFP4: also (amax / 6) / gs for the block scale) put
+// through a rounding to a short format (E2M1, E4M3, a clamped integer)
+// that is monotone in the value.  Here the quotient is formed as a product
+// with a reciprocal, twice, the product nudged down and up by a relative
+// 2^-20: the reciprocal (v_rcp_f32, within 1 ulp; an fp32 division, within
+// 1/2 ulp) and the products add under 2^-21 relative error in all, so the
+// two nudged products bracket the correctly rounded quotient.  Where both
+// round to the same code, so does the quotient; where they differ (a
+// quotient within about 2^-20 of a rounding boundary, an exact tie) the
+// division is done.  This needs the operands in the normal range: the
+// callers take this path only for scales within [2^-100, 2^100]; a product
+// that overflows then stands for a quotient that takes the top code on
+// both sides, one that underflows for one that rounds to zero on both.
 constexpr float kNudgeDown = 1.0f - 0x1p-20f, kNudgeUp = 1.0f + 0x1p-20f;
 
-__device__ __forceinline__ bool nv_in_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
+__device__ __forceinline__ bool in_bracket_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
 // E2M1 codes of x[j] / eff.
 __device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
-  if (nv_in_range(eff)) {
+  if (in_bracket_range(eff)) {
     const float r = __builtin_amdgcn_rcpf(eff);
     const float rl = r * kNudgeDown, rh = r * kNudgeUp;
     Chunk8 lo, hi;
@@ -105,7 +105,7 @@ __device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
 }
 
 // E4M3 code of min((amax / 6) / gs, 448); rgs = 1 / gs (an fp32 division),
-// gs_ok = nv_in_range(gs).
+// gs_ok = in_bracket_range(gs).
 __device__ __forceinline__ uint32_t nv_scale_code(float amax, float gs, float rgs, bool gs_ok) {
   if (gs_ok) {
     const float a = amax * rgs;
@@ -114,6 +114,47 @@ __device__ __forceinline__ uint32_t nv_scale_code(float amax, float gs, float rg
     if (__builtin_expect(cl == ch, 1)) return cl;
   }
   return e4m3_encode(fminf((amax / 6.0f) / gs, 448.0f));
+}
+
+// INT4 codes, clamp(rne(w / s), -8, 7) or, with a zero point z in [-8, 7],
+// clamp(rne(w / s) + z, -8, 7), need no division.  A bf16 value (8
+// significant bits) over an fp16 scale (11) is either exactly a
+// half-integer or at least 2^-12 away from every half-integer: written
+// over a common power of two, a nonzero difference is at least 1/(2b) for
+// the scale's integer significand b < 2^11, or, for quotients of magnitude
+// 1/2 and up, 1/(2a) for the value's significand a < 2^8.  The product
+// y = w (1/s), with v_rcp_f32 (within 1 ulp), is within 2^-18 of the
+// quotient wherever |w/s| <= 16.5.  So after clamping y (to [-8, 7], or
+// [-16, 16] with a zero point; the bounds are integers, and NaN goes to
+// the lower one as fmax drops it), adding 768 rounds it to a multiple of
+// 2^-14: exactly the half-integer in the first case, still on the
+// quotient's side of it in the second.  Adding 1.5 2^23 - 768 then rounds
+// to an integer with ties to even, as rne does to the exact quotient, and
+// leaves that integer in the low bits of the sum.  (Checked exhaustively
+// for every finite bf16 value and every positive finite fp16 scale, with
+// the correctly rounded reciprocal and both its neighbours.)  A scale that
+// overflowed fp16 (+inf) is divided by.
+template <bool ZP>
+__device__ __forceinline__ uint32_t int4_code(float y, int z) {
+  const float c = ZP ? fminf(fmaxf(y, -16.0f), 16.0f) : fminf(fmaxf(y, -8.0f), 7.0f);
+  const int q = (int)(f2u((c + 768.0f) + 12582144.0f) - 0x4B400000u);
+  if constexpr (ZP) return (uint32_t)min(max(q + z, -8), 7) & 0xFu;
+  else return (uint32_t)q & 0xFu;
+}
+
+// Eight INT4 nibbles (element j in bits 4j..4j+3) of x[j] / s, 0 < s.
+template <bool ZP>
+__device__ __forceinline__ uint32_t int4_pack8(const Chunk8& x, float s, int z) {
+  uint32_t p = 0;
+  if (s <= 65504.0f) {
+    const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p |= int4_code<ZP>(x.v[j] * r, z) << (4 * j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p |= int4_code<ZP>(x.v[j] / s, z) << (4 * j);
+  }
+  return p;
 }
 
 template <int LANES>
@@ -160,14 +201,7 @@ __device__ __forceinline__ ZpParams int4zp_params(float lo, float hi) {
 
 // Eight values -> eight INT4 nibbles with the zero point (codes 0 if s == 0).
 __device__ __forceinline__ uint32_t int4zp_pack8(const Chunk8& c, const ZpParams& zp) {
-  uint32_t p = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int qv = 0;
-    if (zp.s != 0.0f) qv = (int)fminf(fmaxf(__builtin_rintf(c.v[j] / zp.s) + zp.z, -8.0f), 7.0f);
-    p |= ((uint32_t)qv & 0xFu) << (4 * j);
-  }
-  return p;
+  return zp.s != 0.0f ? int4_pack8<true>(c, zp.s, (int)zp.z) : 0u;
 }
 
 __device__ __forceinline__ float absmax8(const Chunk8& c) {
@@ -201,7 +235,7 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
     }
   }
   const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
-  const bool gs_ok = FMT == 2 && nv_in_range(gs);
+  const bool gs_ok = FMT == 2 && in_bracket_range(gs);
 
   for (int64_t base = (int64_t)blockIdx.x * kThreads; base < total;
        base += (int64_t)gridDim.x * kThreads) {
@@ -217,16 +251,7 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
     if constexpr (FMT == 0) {
       const uint32_t sbits = fp16_encode(amax / 7.0f);
       const float s = fp16_value(sbits);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int q = 0;
-        if (s != 0.0f) {
-          float qr = __builtin_rintf(x.v[j] / s);
-          qr = fminf(fmaxf(qr, -8.0f), 7.0f);
-          q = (int)qr;
-        }
-        packed |= ((uint32_t)q & 0xFu) << (4 * j);
-      }
+      packed = s != 0.0f ? int4_pack8<false>(x, s, 0) : 0u;
       if (valid && (k0 % G) == 0)
         reinterpret_cast<uint16_t*>(scales)[scale_off<FMT, LAYOUT>(r, k0, cols)] = (uint16_t)sbits;
     } else if constexpr (FMT == 4) {
@@ -285,7 +310,7 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
     }
   }
   const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
-  const bool gs_ok = FMT == 2 && nv_in_range(gs);
+  const bool gs_ok = FMT == 2 && in_bracket_range(gs);
 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -321,20 +346,7 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
     const uint32_t sbits = fp16_encode(amax / 7.0f);
     const float sc = fp16_value(sbits);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t p = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        int qv = 0;
-        if (sc != 0.0f) {
-          float qr = __builtin_rintf(x[i].v[j] / sc);
-          qr = fminf(fmaxf(qr, -8.0f), 7.0f);
-          qv = (int)qr;
-        }
-        p |= ((uint32_t)qv & 0xFu) << (4 * j);
-      }
-      packed[i] = p;
-    }
+    for (int i = 0; i < 4; ++i) packed[i] = sc != 0.0f ? int4_pack8<false>(x[i], sc, 0) : 0u;
     if (store && g == 0) {
       uint16_t* sp = reinterpret_cast<uint16_t*>(scales);
       if constexpr (LAYOUT == kLayoutTiled) sp[((band * Q + q) * 16 + n) * 4 + si] = (uint16_t)sbits;
