@@ -29,6 +29,8 @@
 #include "q4_launch.h"
 #include "q4_layout.h"
 
+#include <string.h>
+
 #pragma clang fp contract(off)
 
 namespace q4 {
@@ -211,15 +213,14 @@ __device__ __forceinline__ float absmax8(const Chunk8& c) {
   return a;
 }
 
-// FMT: 0 INT4 g128, 1 MXFP4, 2 NVFP4.  For NVFP4, gs_src holds either the
-// global scale (gs_is_amax = 0) or the raw bits of the tensor absmax
-// (gs_is_amax = 1).  gs_out (NVFP4, may equal gs_src only when
-// gs_is_amax = 0) receives gs from the first lane.
+// FMT: 0 INT4 g128, 1 MXFP4, 2 NVFP4.  For NVFP4, gs_src holds the global
+// scale, and gs_out, when not null, receives a copy of it from the first
+// lane.
 template <int FMT, int LAYOUT>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
                 uint8_t* __restrict__ codes, void* __restrict__ scales,
-                const float* gs_src, int gs_is_amax, float* gs_out) {
+                const float* gs_src, float* gs_out) {
   constexpr int G = FmtTraits<FMT>::G;
   constexpr int LANES = G / 8;
   const int64_t cpr = cols >> 3;  // chunks of 8 per row
@@ -227,12 +228,8 @@ quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int6
 
   float gs = 0.0f;
   if constexpr (FMT == 2) {
-    if (gs_is_amax) {
-      gs = fmaxf(u2f(*reinterpret_cast<const uint32_t*>(gs_src)), 1e-12f) / 2688.0f;
-    } else {
-      gs = *gs_src;
-      if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
-    }
+    gs = *gs_src;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
   }
   const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
   const bool gs_ok = FMT == 2 && in_bracket_range(gs);
@@ -293,7 +290,7 @@ template <int FMT, int LAYOUT>
 __global__ void __launch_bounds__(kThreads)
 quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
                       uint8_t* __restrict__ codes, void* __restrict__ scales,
-                      const float* gs_src, int gs_is_amax, float* gs_out) {
+                      const float* gs_src, float* gs_out) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[16][512 + 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t KB = (cols + 511) >> 9;
@@ -302,12 +299,8 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
 
   float gs = 0.0f;
   if constexpr (FMT == 2) {
-    if (gs_is_amax) {
-      gs = fmaxf(u2f(*reinterpret_cast<const uint32_t*>(gs_src)), 1e-12f) / 2688.0f;
-    } else {
-      gs = *gs_src;
-      if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
-    }
+    gs = *gs_src;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && gs_out) *gs_out = gs;
   }
   const float rgs = FMT == 2 ? 1.0f / gs : 0.0f;
   const bool gs_ok = FMT == 2 && in_bracket_range(gs);
@@ -412,12 +405,15 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
   }
 }
 
-// Tensor absmax for NVFP4: max |w| over rows x cols, folded into *amax_bits
-// with an atomic max on the fp32 bits (non-negative floats order like their
-// bit patterns, and max is exact, so the result does not depend on order).
+// NVFP4 global scale gs = max(amax, 1e-12) / 2688 of the tensor absmax
+// over rows x cols.  gs is monotone in amax, so the max over workgroups of
+// each one's gs is the gs of the tensor's amax: each workgroup folds its gs
+// into *gs_bits (set beforehand to the gs of amax 0) with an atomic max on
+// the fp32 bits (non-negative floats order like their bit patterns, and max
+// is exact, so the result does not depend on order).
 __global__ void __launch_bounds__(kThreads)
 absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
-              uint32_t* amax_bits) {
+              uint32_t* gs_bits) {
   // rows over workgroups, a row's 16-byte chunks over the threads (no
   // division per element); four independent loads in flight per thread
   const int cpr = (int)(cols >> 3);
@@ -442,16 +438,11 @@ absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_
     float m = part[0];
 #pragma unroll
     for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, part[i]);
-    atomicMax(amax_bits, f2u(m));
+    atomicMax(gs_bits, f2u(fmaxf(m, 1e-12f) / 2688.0f));
   }
 }
 
 __global__ void set_word_kernel(uint32_t* p, uint32_t v) { *p = v; }
-
-// amax bits -> global scale, in place.
-__global__ void finalize_gs_kernel(float* gs) {
-  *gs = fmaxf(u2f(*reinterpret_cast<uint32_t*>(gs)), 1e-12f) / 2688.0f;
-}
 
 // Dequantize: one lane per 8 values; OUT 0 = bf16, 1 = fp32.
 template <int FMT, int OUT, int LAYOUT>
@@ -520,15 +511,15 @@ unsigned grid_for(int64_t chunks) {
 // else the lane-per-8-values kernel.
 template <int FMT, int LAYOUT>
 void launch_q(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols, uint8_t* codes,
-              void* scales, const float* gs_src, int gs_is_amax, float* gs_out, hipStream_t stream) {
+              void* scales, const float* gs_src, float* gs_out, hipStream_t stream) {
   if (cols % 128 == 0) {
     const int64_t blocks = ((stored_rows<LAYOUT>(rows) + 15) / 16) * ((cols + 511) / 512);
     quantize_block_kernel<FMT, LAYOUT><<<(unsigned)blocks, kThreads, 0, stream>>>(
-        src, ld, rows, cols, codes, scales, gs_src, gs_is_amax, gs_out);
+        src, ld, rows, cols, codes, scales, gs_src, gs_out);
   } else {
     const unsigned grid = grid_for(stored_rows<LAYOUT>(rows) * (cols >> 3));
     quantize_kernel<FMT, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales,
-                                                               gs_src, gs_is_amax, gs_out);
+                                                               gs_src, gs_out);
   }
 }
 
@@ -538,33 +529,37 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
                            hipStream_t stream) {
   const int64_t chunks = stored_rows<LAYOUT>(rows) * (cols >> 3);
   if (fmt == 0) {
-    if (chunks) launch_q<0, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
+    if (chunks) launch_q<0, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, nullptr, stream);
   } else if (fmt == 4) {
-    if (chunks) launch_q<4, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
+    if (chunks) launch_q<4, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, nullptr, stream);
   } else if (fmt == 1) {
-    if (chunks) launch_q<1, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, 0, nullptr, stream);
+    if (chunks) launch_q<1, LAYOUT>(src, ld, rows, cols, codes, scales, nullptr, nullptr, stream);
   } else {
     if (gs_in) {
       if (chunks) {
-        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs_in, 0, gs, stream);
+        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs_in, gs, stream);
       } else {
         // nothing to quantize: still record the caller's gs
         hipError_t e = hipMemcpyAsync(gs, gs_in, sizeof(float), hipMemcpyDeviceToDevice, stream);
         if (e != hipSuccess) return e;
       }
     } else {
-      uint32_t* amax = reinterpret_cast<uint32_t*>(gs);
-      set_word_kernel<<<1, 1, 0, stream>>>(amax, 0u);
+      // gs of amax 0 (an empty tensor keeps it), then the absmax pass folds
+      // each workgroup's gs into it, and the quantizer reads the result
+      const float gs0 = 1e-12f / 2688.0f;
+      uint32_t gs0_bits = 0;
+      memcpy(&gs0_bits, &gs0, sizeof gs0_bits);
+      uint32_t* gs_bits = reinterpret_cast<uint32_t*>(gs);
+      set_word_kernel<<<1, 1, 0, stream>>>(gs_bits, gs0_bits);
       if (chunks) {
         if (rows > 0 && cols > 0) {
           // one workgroup per CU: with 2048 workgroups the final atomic max
           // of each one serialized into a tail (8192^2 NVFP4: 82 -> 69 us)
           const unsigned agrid = (unsigned)(rows < 256 ? rows : 256);
-          absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, amax);
+          absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, gs_bits);
         }
-        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, 1, nullptr, stream);
+        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, nullptr, stream);
       }
-      finalize_gs_kernel<<<1, 1, 0, stream>>>(gs);
     }
   }
   return hipGetLastError();
