@@ -47,8 +47,10 @@ def fp8_inputs(rows, cols, seed):
 
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
 @pytest.mark.parametrize("rows,cols", [(1, 512), (5, 1024), (17, 512), (130, 2048), (64, 4096),
-                                       (3, 96), (40, 208)])
+                                       (3, 96), (40, 208), (7, 8192), (3, 8704), (2, 16384)])
 def test_fp8_rows_quantize_bit_exact(rows, cols, layout):
+    """Rows up to 8192 values are quantized by a workgroup holding the row
+    in registers; longer ones (8704, 16384) by a wave reading it twice."""
     if layout == "tiled" and cols % 512:
         pytest.skip("the tiled layout needs cols % 512 == 0")
     log("fp8 quantize", layout, rows, cols)
@@ -73,6 +75,58 @@ def test_fp8_rows_quantize_bit_exact(rows, cols, layout):
     assert np.array_equal(d32.cpu().numpy().view(np.uint32), ref.view(np.uint32))
     exp16 = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(ref))
     assert np.array_equal(d16.cpu().float().numpy().view(np.uint32), exp16.view(np.uint32))
+
+
+def _fp8_quantize_matches_oracle(a: torch.Tensor, layout="rows"):
+    rows, cols = a.shape
+    qg = q4.quantize(a.to(DEV), "fp8_row", layout=layout)
+    torch.cuda.synchronize()
+    qr = oracle.quantize_fp8_rows(to_f32(a))
+    codes = qg.codes.cpu().numpy()
+    if layout == "tiled":
+        codes, _ = fp8_untile(codes, rows, cols)
+    bad = np.argwhere(codes != qr.codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+    assert np.array_equal(qg.scales.cpu().numpy(), qr.scales)
+
+
+@pytest.mark.parametrize("width", (512, 1024, 4096))
+def test_fp8_rows_quantize_all_bf16_values(width):
+    """Every finite bf16 value, sorted by magnitude into rows of `width` (1,
+    2 and 8 octaves below each row's largest value, so the quotients cover
+    the normal E4M3 codes and, for the widest rows, the subnormal ones), with
+    random signs, in random order within each row."""
+    bits = np.arange(0, 1 << 16, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    v = np.sort(np.abs(v[np.isfinite(v)]))[::-1]
+    n = (v.size // width) * width
+    rng = np.random.default_rng(81)
+    x = (v[:n] * np.where(rng.random(n) < 0.5, -1, 1)).reshape(-1, width).astype(np.float32)
+    x = rng.permuted(x, axis=1)
+    log("fp8 all bf16", x.shape)
+    for layout in ("rows", "tiled"):
+        _fp8_quantize_matches_oracle(torch.from_numpy(x).to(torch.bfloat16), layout)
+
+
+def test_fp8_rows_quantize_exact_ties():
+    """Rows whose largest magnitude is 448 2^e have scale 2^e exactly; their
+    other values are the midpoints between consecutive E4M3 values (the
+    subnormal ones (2k+1) 2^-10 and the normal ones up to 448) times 2^e, of
+    both signs: ties, which go to the even code."""
+    e4m3 = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)  # 0 .. 448
+    mids = ((e4m3[:-1] + e4m3[1:]) / 2).astype(np.float32)
+    rows = []
+    for e in range(-8, 8):
+        row = np.zeros(512, np.float32)
+        row[0] = 448.0 * 2.0 ** e
+        row[1:1 + mids.size] = mids * 2.0 ** e
+        row[1 + mids.size:1 + 2 * mids.size] = -mids * 2.0 ** e
+        rows.append(row)
+    x = np.stack(rows)
+    a = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(to_f32(a), x)  # every midpoint is exact in bf16
+    for layout in ("rows", "tiled"):
+        _fp8_quantize_matches_oracle(a, layout)
 
 
 def _w4a8_case(M, N, K, alayout, wlayout, seed):

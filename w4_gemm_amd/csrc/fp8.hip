@@ -34,6 +34,79 @@ __device__ __forceinline__ uint32_t fp8_code(float x, float s) {
   return ((f2u(y) >> 24) & 0x80u) | e4m3_encode(t);
 }
 
+// Element of a group of eight stored at byte i of the two output words:
+// row-major keeps the order; the tiled layout puts the even elements in
+// the first word and the odd ones in the second.
+template <int LAYOUT>
+__device__ __forceinline__ int fp8_slot(int i) {
+  return LAYOUT == kLayoutRows ? i : (i & 3) * 2 + (i >> 2);
+}
+
+// Four E4M3 codes per word.  v_cvt_pk_fp8_f32 rounds to the nearest E4M3
+// value with ties to the even code and keeps the sign (-0 -> 0x80); its
+// inputs here are already clamped to +-448.
+__device__ __forceinline__ uint2 fp8_cvt8(const float (&f)[8]) {
+  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], w0, true);
+  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], w1, true);
+  return make_uint2(w0, w1);
+}
+
+// Codes of x[0..7] / s in the layout's byte order.  The quotient is
+// bracketed by the products with the reciprocal nudged down and up by a
+// relative 2^-20 (rl, rh; v_rcp_f32 is within 1 ulp and each product adds
+// at most 1/2 ulp, far less than the nudge); the clamp to +-448 and the
+// E4M3 rounding are monotone in the value, so where both ends give the
+// same codes, so does the quotient.  Otherwise (a quotient within about
+// 2^-20 of a rounding boundary, an exact tie), and for scales outside
+// [2^-100, 2^100], the eight values are divided.
+template <int LAYOUT>
+__device__ __forceinline__ uint2 fp8_pack8(const float (&x)[8], float s, float rl, float rh, bool fast) {
+  if (fast) {
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = x[fp8_slot<LAYOUT>(i)];
+      lo[i] = fminf(fmaxf(v * rl, -448.0f), 448.0f);
+      hi[i] = fminf(fmaxf(v * rh, -448.0f), 448.0f);
+    }
+    const uint2 pl = fp8_cvt8(lo), ph = fp8_cvt8(hi);
+    if (__builtin_expect(pl.x == ph.x && pl.y == ph.y, 1)) return pl;
+  }
+  uint32_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = fp8_code(x[fp8_slot<LAYOUT>(i)], s);
+  return make_uint2(e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24),
+                    e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24));
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void fp8_store8(uint8_t* codes, int64_t r, int64_t k0, int64_t cols, uint2 w) {
+  if constexpr (LAYOUT == kLayoutRows) {
+    *reinterpret_cast<uint2*>(codes + r * cols + k0) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 0)) = w.x;
+    *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 1)) = w.y;
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+  x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+  x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float absmax_bf16x8(const uint4& v, float a) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+  return a;
+}
+
+// One wave per row, any length: the row is read twice (amax, then encode;
+// the second read mostly hits the cache).
 template <int LAYOUT>
 __global__ void __launch_bounds__(64 * kRowsPerBlock)
 fp8_rows_quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
@@ -42,45 +115,75 @@ fp8_rows_quantize_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t r
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= srows) return;
   if (r >= rows) {  // padding row of the last tile: zero codes
-    for (int64_t k0 = (int64_t)lane * 8; k0 < cols; k0 += 512) {
-      *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 0)) = 0u;
-      *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 1)) = 0u;
-    }
+    for (int64_t k0 = (int64_t)lane * 8; k0 < cols; k0 += 512) fp8_store8<LAYOUT>(codes, r, k0, cols, make_uint2(0, 0));
     return;
   }
   const uint16_t* row = src + r * ld;
-  // pass 1: the row's largest magnitude (exact: max of bf16 values)
-  float amax = 0.0f;
-  for (int64_t k0 = (int64_t)lane * 8; k0 < cols; k0 += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
-  }
+  float amax = 0.0f;  // the row's largest magnitude (exact: max of bf16 values)
+  for (int64_t k0 = (int64_t)lane * 8; k0 < cols; k0 += 512)
+    amax = absmax_bf16x8(*reinterpret_cast<const uint4*>(row + k0), amax);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const float s = fmaxf(amax, 1e-12f) / 448.0f;
   if (lane == 0) scales[r] = s;
-  // pass 2: encode (the row is re-read from cache)
+  const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+  const float rcp = __builtin_amdgcn_rcpf(s);
+  const float rl = rcp * (1.0f - 0x1p-20f), rh = rcp * (1.0f + 0x1p-20f);
+  float x[8];
   for (int64_t k0 = (int64_t)lane * 8; k0 < cols; k0 += 512) {
-    const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t e[8];
+    unpack8(*reinterpret_cast<const uint4*>(row + k0), x);
+    fp8_store8<LAYOUT>(codes, r, k0, cols, fp8_pack8<LAYOUT>(x, s, rl, rh, fast));
+  }
+}
+
+// One workgroup of 256 threads per row of at most 256 * 8 * kWgChunks
+// values: thread t holds chunks t, t + 256, ... (each 8 values, 16 bytes)
+// in registers, every load issued before the first is used, so the row is
+// read from HBM once; the row max is combined over the four waves in LDS.
+constexpr int kWgChunks = 4;
+
+template <int LAYOUT>
+__global__ void __launch_bounds__(256)
+fp8_rows_quantize_wg_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+                            uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  if (r >= rows) {  // padding row of the last tile: zero codes
+    for (int64_t k0 = (int64_t)tid * 8; k0 < cols; k0 += 2048) fp8_store8<LAYOUT>(codes, r, k0, cols, make_uint2(0, 0));
+    return;
+  }
+  const uint16_t* row = src + r * ld;
+  // every load unconditional, so that all are in flight together: a chunk
+  // past the row's end re-reads the row's first one (cols >= 16), which
+  // leaves the max unchanged and is never encoded
+  uint4 v[kWgChunks];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      e[2 * j] = fp8_code(bf16_lo(w[j]), s);
-      e[2 * j + 1] = fp8_code(bf16_hi(w[j]), s);
-    }
-    if constexpr (LAYOUT == kLayoutRows) {
-      uint2 o;
-      o.x = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-      o.y = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
-      *reinterpret_cast<uint2*>(codes + r * cols + k0) = o;
-    } else {
-      *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 0)) =
-          e[0] | (e[2] << 8) | (e[4] << 16) | (e[6] << 24);
-      *reinterpret_cast<uint32_t*>(codes + fp8_tiled_dword(r, k0, cols, 1)) =
-          e[1] | (e[3] << 8) | (e[5] << 16) | (e[7] << 24);
+  for (int i = 0; i < kWgChunks; ++i) {
+    const int64_t k0 = (int64_t)(tid + 256 * i) * 8;
+    v[i] = *reinterpret_cast<const uint4*>(row + (k0 < cols ? k0 : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first use
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kWgChunks; ++i) amax = absmax_bf16x8(v[i], amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float part[4];
+  if ((tid & 63) == 0) part[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float s = fmaxf(amax, 1e-12f) / 448.0f;
+  if (tid == 0) scales[r] = s;
+  const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+  const float rcp = __builtin_amdgcn_rcpf(s);
+  const float rl = rcp * (1.0f - 0x1p-20f), rh = rcp * (1.0f + 0x1p-20f);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < kWgChunks; ++i) {
+    const int64_t k0 = (int64_t)(tid + 256 * i) * 8;
+    if (k0 < cols) {
+      unpack8(v[i], x);
+      fp8_store8<LAYOUT>(codes, r, k0, cols, fp8_pack8<LAYOUT>(x, s, rl, rh, fast));
     }
   }
 }
@@ -141,13 +244,20 @@ hipError_t launch_fp8_rows_quantize(int layout, const uint16_t* src, int64_t ld,
                                     int64_t cols, uint8_t* codes, float* scales, hipStream_t stream) {
   const int64_t srows = layout == kLayoutTiled ? ((rows + 15) >> 4) << 4 : rows;
   if (srows == 0 || cols == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((srows + kRowsPerBlock - 1) / kRowsPerBlock);
-  if (layout == kLayoutTiled)
-    fp8_rows_quantize_kernel<kLayoutTiled><<<grid, 64 * kRowsPerBlock, 0, stream>>>(src, ld, rows, cols, srows,
-                                                                                  codes, scales);
-  else
-    fp8_rows_quantize_kernel<kLayoutRows><<<grid, 64 * kRowsPerBlock, 0, stream>>>(src, ld, rows, cols, srows,
-                                                                                 codes, scales);
+  if (cols <= 2048 * kWgChunks) {  // a workgroup per row, the row in registers
+    if (layout == kLayoutTiled)
+      fp8_rows_quantize_wg_kernel<kLayoutTiled><<<(unsigned)srows, 256, 0, stream>>>(src, ld, rows, cols, codes, scales);
+    else
+      fp8_rows_quantize_wg_kernel<kLayoutRows><<<(unsigned)srows, 256, 0, stream>>>(src, ld, rows, cols, codes, scales);
+  } else {  // a wave per row, two passes
+    const unsigned grid = (unsigned)((srows + kRowsPerBlock - 1) / kRowsPerBlock);
+    if (layout == kLayoutTiled)
+      fp8_rows_quantize_kernel<kLayoutTiled><<<grid, 64 * kRowsPerBlock, 0, stream>>>(src, ld, rows, cols, srows,
+                                                                                    codes, scales);
+    else
+      fp8_rows_quantize_kernel<kLayoutRows><<<grid, 64 * kRowsPerBlock, 0, stream>>>(src, ld, rows, cols, srows,
+                                                                                   codes, scales);
+  }
   return hipGetLastError();
 }
 
