@@ -47,10 +47,12 @@ def fp8_inputs(rows, cols, seed):
 
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
 @pytest.mark.parametrize("rows,cols", [(1, 512), (5, 1024), (17, 512), (130, 2048), (64, 4096),
-                                       (3, 96), (40, 208), (7, 8192), (3, 8704), (2, 16384)])
+                                       (3, 96), (40, 208), (7, 8192), (3, 8704), (2, 16384),
+                                       (2050, 1024), (2048, 8192)])
 def test_fp8_rows_quantize_bit_exact(rows, cols, layout):
     """Rows up to 8192 values are quantized by a workgroup holding the row
-    in registers; longer ones (8704, 16384) by a wave reading it twice."""
+    in registers; longer ones (8704, 16384) by a wave reading it twice;
+    2050 rows end in a ragged tile."""
     if layout == "tiled" and cols % 512:
         pytest.skip("the tiled layout needs cols % 512 == 0")
     log("fp8 quantize", layout, rows, cols)
