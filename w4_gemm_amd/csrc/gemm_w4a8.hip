@@ -16,9 +16,12 @@
 // INT4 group exactly.
 //
 // Tiled kernel (both operands in the tiled layouts, K % 512 == 0):
-//   * a workgroup of 8 waves computes a 256 x 256 block of C; wave (wm, wn)
-//     owns 128 x 64 = 8 x 4 matrix-core tiles (128 fp32 accumulators), the
-//     INT4->E4M3 conversion of each weight fragment feeding 8 products;
+//   * a workgroup of 8 waves computes a 256 x 256 block of C; wave w owns
+//     all 256 rows and the 32 columns of weight tiles 2w, 2w+1 = 16 x 2
+//     matrix-core tiles (128 fp32 accumulators), so every weight tile is
+//     converted INT4->E4M3 by one wave only and each converted fragment
+//     feeds 16 products (a 2 x 4 arrangement of 128 x 64 wave tiles converted
+//     every tile twice and measured 6% slower);
 //   * K advances in stages of 128: 16 FP8 A tiles (2 KB each) and 16 INT4 W
 //     tiles (1 KB) are copied verbatim into LDS by direct global->LDS loads
 //     (6 per wave per stage), two stages ahead, into three buffers; the W
@@ -99,7 +102,7 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wn = wave;  // the wave's two weight tiles 2wn, 2wn+1; all 16 A tiles
   const int S = K >> 7, Q = K >> 9;
   const int RTA = (M + 15) >> 4, RTW = (N + 15) >> 4;
 
@@ -146,29 +149,29 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
     copy4_to_lds(ssrc + (int64_t)q * 128, &sbuf[(t >> 2) & 1][256 * wave]);
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[16][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](int s, int j) {
     const int bi = s % kBufs;
     // A fragment i: operand bytes 0..15 and 16..31 of the lane
     auto load_a = [&](int i) {
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&abuf[bi][wm * 8 + i][lane * 16]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&abuf[bi][wm * 8 + i][1024 + lane * 16]);
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&abuf[bi][i][lane * 16]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&abuf[bi][i][1024 + lane * 16]);
       return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
     };
     // the weight fragments, converted to E4M3, and the fp16 scale of group
     // 4q + j of the lane's weight column in each (scale tile: [row][group])
-    float sw[4];
-    i32x8_t wq[4];
+    float sw[2];
+    i32x8_t wq[2];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < 2; ++jj) {
       sw[jj] = fp16_value(*reinterpret_cast<const uint16_t*>(
-          &sbuf[(s >> 2) & 1][(wn * 4 + jj) * 128 + (lane & 15) * 8 + j * 2]));
-      wq[jj] = int4_frag_to_e4m3(*reinterpret_cast<const u32x4_t*>(&wbuf[bi][wn * 4 + jj][lane * 16]));
+          &sbuf[(s >> 2) & 1][(wn * 2 + jj) * 128 + (lane & 15) * 8 + j * 2]));
+      wq[jj] = int4_frag_to_e4m3(*reinterpret_cast<const u32x4_t*>(&wbuf[bi][wn * 2 + jj][lane * 16]));
     }
     i32x8_t a[2];
     a[0] = load_a(0);
@@ -176,11 +179,11 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
     // compiler from hoisting every fragment load, which would not fit the
     // register budget of two waves per SIMD)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < 7) a[(i + 1) & 1] = load_a(i + 1);
+    for (int i = 0; i < 16; ++i) {
+      if (i < 15) a[(i + 1) & 1] = load_a(i + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < 2; ++jj) {
         const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             a[i & 1], wq[jj], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
@@ -218,17 +221,17 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
   wait_vmcnt<0>();
 
   // lane l, register r of tile (i, jj) holds row 4(l/16) + r, column l%16
-  const int row0 = bm * 256 + wm * 128;
-  const int col0 = bn * 256 + wn * 64 + (lane & 15);
+  const int row0 = bm * 256;
+  const int col0 = bn * 256 + wn * 32 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = row0 + i * 16 + 4 * (lane >> 4) + r;
       if (m >= M) continue;
       const float sa = a_scales[m];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < 2; ++jj) {
         const int n = col0 + jj * 16;
         if (n < N) C[(int64_t)m * ldc + n] = (uint16_t)f32_to_bf16_rne(acc[i][jj][r] * sa);
       }
