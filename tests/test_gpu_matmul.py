@@ -231,7 +231,7 @@ def test_strided_operands_match_contiguous(fmt, layout):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(200, 300, 512), (64, 256, 128), (1, 1000, 1024), (333, 520, 1152),
-                                   (130, 1030, 2048), (256, 512, 4096)])
+                                   (130, 1030, 2048), (256, 512, 4096), (600, 700, 1024)])
 def test_gemm_w4a16_small(fmt, M, N, K, layout):
     if layout == "tiled" and not tiled_ok(K):
         pytest.skip("the tiled layout needs K % 512 == 0")

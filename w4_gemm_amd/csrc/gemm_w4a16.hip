@@ -15,19 +15,22 @@
 // a[m][32g + 8i + (0..8)] with m = l%16.
 //
 // Work decomposition:
-//   * a workgroup of 8 waves computes a 128 x 512 block of C.  All waves
-//     share the 128 activation rows; wave w owns the 64 columns of weight
-//     tiles 4w..4w+3: 8 x 4 matrix-core tiles, 128 fp32 accumulators per
-//     lane (two waves per SIMD).  Each dequantized weight fragment feeds 8
+//   * a workgroup of 8 waves computes a 256 x 256 block of C.  All waves
+//     share the 256 activation rows; wave w owns the 32 columns of weight
+//     tiles 2w, 2w+1: 16 x 2 matrix-core tiles, 128 fp32 accumulators per
+//     lane (two waves per SIMD).  Each dequantized weight fragment feeds 16
 //     matrix instructions, which keeps the dequantization (a multiply per
-//     value for NVFP4) off the critical path.
+//     value for NVFP4) small next to the matrix work (a 128 x 512 block
+//     with 8 x 4 tiles per wave, 8 products per fragment, measured 18%
+//     slower on NVFP4 4096 x 8192 x 8192).  The activation fragments are
+//     read from LDS four row tiles at a time, one group ahead.
 //   * K advances in stages of 64 (half a super-chunk: steps 2h, 2h+1).  The
-//     activations of a stage (128 rows x 64 k, 16 KB) are gathered into LDS
+//     activations of a stage (256 rows x 64 k, 32 KB) are gathered into LDS
 //     by direct global->LDS loads in matrix-fragment order -- each load
 //     instruction fills one fragment, lane l fetching exactly the 16 bytes
 //     it will later read -- so every fragment read is one contiguous,
 //     conflict-free kilobyte.  Three buffers, two stages ahead.
-//   * the weight tiles of a super-chunk (the wave's own four, 1 KB each) are
+//   * the weight tiles of a super-chunk (the wave's own two, 1 KB each) are
 //     copied verbatim into LDS one super-chunk ahead (two buffers); the
 //     scale words of a group of four super-chunks go straight into registers
 //     (two sets).
@@ -48,17 +51,20 @@ namespace q4 {
 namespace {
 
 constexpr int kWaves = 8;
-constexpr int kRowTiles = 8;                    // 16-row activation tiles per block (128 rows)
-constexpr int kColTiles = 4 * kWaves;           // 16-column weight tiles per block (512 cols)
+constexpr int kRowTiles = 16;                   // 16-row activation tiles per block (256 rows)
+constexpr int kWTiles = 2;                      // weight tiles per wave
+constexpr int kColTiles = kWTiles * kWaves;     // 16-column weight tiles per block (256 cols)
 constexpr int kAFrags = 2 * kRowTiles;          // activation fragments per stage
 constexpr int kABufs = 3;
-constexpr size_t kSmemBytes = kABufs * kAFrags * 1024 + 2 * kColTiles * 1024;  // 112 KB
+constexpr size_t kSmemBytes = kABufs * kAFrags * 1024 + 2 * kColTiles * 1024;  // 128 KB
 
 // Loads issued for running stage v (group v): the stage's activation
-// fragments (2 per wave), the weight tiles of super-chunk v/2 when v is
-// even (4 per wave), the scale words of scale group v/8 when v % 8 == 0
-// (4 per wave).
-constexpr int group_loads(int v) { return 2 + (v % 2 == 0 ? 4 : 0) + (v % 8 == 0 ? 4 : 0); }
+// fragments (4 per wave), the weight tiles of super-chunk v/2 when v is
+// even (2 per wave), the scale words of scale group v/8 when v % 8 == 0
+// (2 per wave).
+constexpr int group_loads(int v) {
+  return kAFrags / kWaves + (v % 2 == 0 ? kWTiles : 0) + (v % 8 == 0 ? kWTiles : 0);
+}
 
 template <int FMT>
 __global__ void __launch_bounds__(kWaves * 64)
@@ -76,32 +82,36 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
   const int S = K >> 7, Q = K >> 9, S2 = 2 * S;   // super-chunks, scale groups, stages
   const int RTW = (N + 15) >> 4;
 
-  // workgroup -> 128 x 512 block of C: XCD-major, then groups of 4 block rows
-  const int TM = (M + 127) >> 7, TN = (N + 511) >> 9, T = TM * TN;
+  // workgroup -> 256 x 256 block of C: XCD-major, then groups of 4 block rows
+  const int TM = (M + 255) >> 8, TN = (N + 255) >> 8, T = TM * TN;
   const int b = blockIdx.x;
   const int lin = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
   const int gsz = 4 * TN, first_m = (lin / gsz) * 4, gm = min(TM - first_m, 4);
   const int bm = first_m + (lin % gsz) % gm, bn = (lin % gsz) / gm;
 
-  // activation copies: this wave fills the fragments of row tile `wave`
-  // (steps 2h and 2h+1 of each stage); lane l reads row 16*wave + l%16
-  // (clamped) at k = 32(l/16) + 8i within the super-chunk
-  const int arow = min(bm * 128 + 16 * wave + (lane & 15), M - 1);
-  const uint16_t* asrc = A + (int64_t)arow * lda + 32 * (lane >> 4);
-  // this wave's weight tiles (copied and multiplied by it alone)
-  const int wt0 = bn * kColTiles + 4 * wave;
-  // (wave-uniform bases; the lane offsets are added at each load)
-  const uint8_t* wsrc[4];
+  // activation copies: this wave fills the fragments of row tiles 2*wave
+  // and 2*wave+1 (steps 2h and 2h+1 of each stage); lane l reads row
+  // 16*tile + l%16 (clamped) at k = 32(l/16) + 8i within the super-chunk
+  const uint16_t* asrc[2];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) wsrc[jj] = codes + (int64_t)min(wt0 + jj, RTW - 1) * S * 1024;
+  for (int t = 0; t < 2; ++t) {
+    const int arow = min(bm * 256 + 16 * (2 * wave + t) + (lane & 15), M - 1);
+    asrc[t] = A + (int64_t)arow * lda + 32 * (lane >> 4);
+  }
+  // this wave's weight tiles (copied and multiplied by it alone)
+  const int wt0 = bn * kColTiles + kWTiles * wave;
+  // (wave-uniform bases; the lane offsets are added at each load)
+  const uint8_t* wsrc[kWTiles];
+#pragma unroll
+  for (int jj = 0; jj < kWTiles; ++jj) wsrc[jj] = codes + (int64_t)min(wt0 + jj, RTW - 1) * S * 1024;
   const int wlane = lane * 16;
   // this lane's scale bytes of a scale group for weight tile jj: MXFP4 4
   // bytes (one per super-chunk), NVFP4 8 (two per super-chunk), INT4 4 fp16
   // of row n = lane%16 (one per super-chunk)
   constexpr int SW = FMT == 1 ? 1 : FMT == 4 ? 4 : 2;  // 32-bit words per tile and group
-  const uint8_t* ssrc[4];
+  const uint8_t* ssrc[kWTiles];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < kWTiles; ++jj) {
     const int64_t t = min(wt0 + jj, RTW - 1);
     ssrc[jj] = scales + t * Q * (FMT == 0 ? 128 : FMT == 1 || FMT == 4 ? 256 : 512);
   }
@@ -110,23 +120,25 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
 
   // scale words of the current scale group and of the next one (loaded
   // with group 8q, moved into place when the group's first stage starts)
-  uint32_t scur[4][SW], snext[4][SW];
+  uint32_t scur[kWTiles][SW], snext[kWTiles][SW];
   auto issue = [&](int v, auto jc) {  // group v; jc = v % 8
     constexpr int J = decltype(jc)::value;
     const int vs = min(v, S2 - 1);
     const int s = vs >> 1, h = vs & 1;
 #pragma unroll
-    for (int ip = 0; ip < 2; ++ip)
-      copy16_to_lds(asrc + 128 * s + 8 * (2 * h + ip), abuf[v % kABufs][2 * wave + ip]);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ip = 0; ip < 2; ++ip)
+        copy16_to_lds(asrc[t] + 128 * s + 8 * (2 * h + ip), abuf[v % kABufs][2 * (2 * wave + t) + ip]);
     if constexpr (J % 2 == 0) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        copy16_to_lds(wsrc[jj] + (int64_t)s * 1024 + wlane, wbuf[(v >> 1) & 1][4 * wave + jj]);
+      for (int jj = 0; jj < kWTiles; ++jj)
+        copy16_to_lds(wsrc[jj] + (int64_t)s * 1024 + wlane, wbuf[(v >> 1) & 1][kWTiles * wave + jj]);
     }
     if constexpr (J == 0) {
       const int q = min(v >> 3, Q - 1);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < kWTiles; ++jj) {
         if constexpr (SW == 1) {
           snext[jj][0] = *reinterpret_cast<const uint32_t*>(ssrc[jj] + (int64_t)q * 256 + slane);
         } else if constexpr (SW == 4) {
@@ -142,12 +154,12 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
     }
   };
 
-  f32x4_t acc[kRowTiles][4];
+  f32x4_t acc[kRowTiles][kWTiles];
 #pragma unroll
   for (int i = 0; i < kRowTiles; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  u32x4_t wq[4];  // the wave's weight fragments of the current super-chunk
+    for (int jj = 0; jj < kWTiles; ++jj) acc[i][jj] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4_t wq[kWTiles];  // the wave's weight fragments of the current super-chunk
 
   // stage u, J = u % 8: wait until only group u+1 may be outstanding,
   // barrier, issue group u+2 (into the buffers stage u-1 used), multiply.
@@ -159,22 +171,22 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
     stage_barrier();
     if constexpr (J == 0) {  // group u/8's scale words have landed (group u is done)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < kWTiles; ++jj)
 #pragma unroll
         for (int w = 0; w < SW; ++w) scur[jj][w] = snext[jj][w];
     }
     issue(u + 2, std::integral_constant<int, (J + 2) % 8>());
     if constexpr (H == 0) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        wq[jj] = *reinterpret_cast<const u32x4_t*>(&wbuf[(u >> 1) & 1][4 * wave + jj][lane * 16]);
+      for (int jj = 0; jj < kWTiles; ++jj)
+        wq[jj] = *reinterpret_cast<const u32x4_t*>(&wbuf[(u >> 1) & 1][kWTiles * wave + jj][lane * 16]);
     }
 #pragma unroll
     for (int ip = 0; ip < 2; ++ip) {
       const int i = 2 * H + ip;      // matrix step within the super-chunk
-      bf16x8_t wb[4];
+      bf16x8_t wb[kWTiles];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < kWTiles; ++jj) {
         if constexpr (FMT == 0) {
           const uint32_t hw = (scur[jj][SI >> 1] >> (16 * (SI & 1))) & 0xFFFFu;
           wb[jj] = dq8_int4(wq[jj][i], fp16_value(hw));
@@ -190,11 +202,27 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
           wb[jj] = dq8_e2m1_mul(wq[jj][i], e4m3_value(sb) * gs);
         }
       }
+      // the activation fragments in groups of four row tiles, one group
+      // read ahead of the products (the fences keep the compiler from
+      // reading all sixteen at once, which would not fit two waves per SIMD)
+      constexpr int RG = 4;
+      bf16x8_t af[2][RG];
+      auto read_a = [&](bf16x8_t (&dst)[RG], int g) {
 #pragma unroll
-      for (int r = 0; r < kRowTiles; ++r) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&abuf[u % kABufs][2 * r + ip][lane * 16]));
+        for (int q = 0; q < RG; ++q)
+          dst[q] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(&abuf[u % kABufs][2 * (RG * g + q) + ip][lane * 16]));
+      };
+      read_a(af[0], 0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[r][jj] = mma16x16x32(wb[jj], a, acc[r][jj]);
+      for (int g = 0; g < kRowTiles / RG; ++g) {
+        if (g + 1 < kRowTiles / RG) read_a(af[(g + 1) & 1], g + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < RG; ++q)
+#pragma unroll
+          for (int jj = 0; jj < kWTiles; ++jj)
+            acc[RG * g + q][jj] = mma16x16x32(wb[jj], af[g & 1][q], acc[RG * g + q][jj]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -216,15 +244,15 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
 
   // tile (r, jj): lane l, register q holds C[m][n] with m = 16r + l%16 and
   // n = 16jj + 4(l/16) + q -- four consecutive columns of one row
-  const int m0 = bm * 128 + (lane & 15);
-  const int n0 = bn * 512 + 64 * wave + 4 * (lane >> 4);
+  const int m0 = bm * 256 + (lane & 15);
+  const int n0 = bn * 256 + 16 * kWTiles * wave + 4 * (lane >> 4);
 #pragma unroll
   for (int r = 0; r < kRowTiles; ++r) {
     const int m = m0 + 16 * r;
     if (m < M) {
       uint16_t* crow = C + (int64_t)m * ldc;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < kWTiles; ++jj) {
         const int n = n0 + 16 * jj;
         const f32x4_t v = acc[r][jj];
         if (n + 3 < N) {
@@ -244,7 +272,7 @@ hipError_t run(const uint16_t* A, int64_t lda, int64_t M, const uint8_t* codes, 
                const float* gs, int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
   const hipError_t attr = set_max_lds<&w4a16_tiled_kernel<FMT>>(kSmemBytes);
   if (attr != hipSuccess) return attr;
-  const int64_t T = ((M + 127) / 128) * ((N + 511) / 512);
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
   w4a16_tiled_kernel<FMT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(
       A, lda, (int)M, codes, static_cast<const uint8_t*>(scales), gs, (int)N, (int)K, C, ldc);
   return hipGetLastError();
