@@ -24,19 +24,20 @@
 // E4M3 * gs by at most one fp32 rounding).
 //
 // Two kernels:
-//   * both operands in the tiled layout: a workgroup of 4 x 2 waves computes
-//     a 256 x 128 block of C, each wave a 64 x 64 part (4 x 4 tiles of
-//     16x16); each matrix step dequantizes 4 A and 4 W fragments (8 codes
-//     per lane each) for 16 matrix instructions, two waves per SIMD
-//     overlapping one's dequantization with the other's matrix work.  (One
-//     wave per SIMD with 64 x 128 or 128 x 64 per wave, fewer dequantized
-//     fragments per matrix instruction, measured 4-5% slower; 128 x 128 per
-//     wave does not fit the registers.)  K advances one super-chunk (128 k)
-//     per stage; the stage's 24 code tiles (1 KB each) are copied verbatim
-//     into LDS by direct global->LDS loads, two stages ahead, into three
-//     buffers, and the E4M3 scales (512 bytes per tile and group of four
-//     super-chunks) into two buffers -- the copy scheme of the MXFP4 W4A4
-//     kernel.
+//   * both operands in the tiled layout: a workgroup of 2 x 4 waves computes
+//     a 256 x 256 block of C, each wave a 128 x 64 part (8 x 4 tiles of
+//     16x16); each matrix step dequantizes 8 A and 4 W fragments (8 codes
+//     per lane each) for 32 matrix instructions, two waves per SIMD
+//     overlapping one's dequantization with the other's matrix work.  The
+//     codes are read from LDS one matrix step at a time (a dword per tile),
+//     which keeps the registers within two waves per SIMD.  (4 x 2 waves of
+//     64 x 64, 8 fragments per 16 matrix instructions, measured 9.5%
+//     slower; 128 x 128 per wave does not fit the registers.)  K advances one
+//     super-chunk (128 k) per stage; the stage's 32 code tiles (1 KB each)
+//     are copied verbatim into LDS by direct global->LDS loads, two stages
+//     ahead, into three buffers, and the E4M3 scales (512 bytes per tile and
+//     group of four super-chunks) into two buffers -- the copy scheme of the
+//     MXFP4 W4A4 kernel.
 //   * any other layout combination: a register-tiled kernel (4 waves, 64 x
 //     64 of C per wave) loading each lane's 16 code bytes per super-chunk and
 //     its two scale bytes directly.
@@ -187,29 +188,33 @@ w4a4nv_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
     constexpr int j = decltype(jc)::value;
     const uint8_t(*cb)[1024] = cbuf[s % kCodeBufs];
     const uint8_t(*sb)[kScaleGroup] = sbuf[(s >> 2) & 1];
-    u32x4_t va[TM], vw[TN];
     f16x2_t fa[TM], fw[TN];  // the lane's two block scales of this stage per tile
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      va[i] = *reinterpret_cast<const u32x4_t*>(&cb[wm * TM + i][lane * 16]);
+    for (int i = 0; i < TM; ++i)
       fa[i] = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sb[wm * TM + i][lane * 8 + 2 * j]));
-    }
 #pragma unroll
-    for (int jj = 0; jj < TN; ++jj) {
-      vw[jj] = *reinterpret_cast<const u32x4_t*>(&cb[kBMT + wn * TN + jj][lane * 16]);
+    for (int jj = 0; jj < TN; ++jj)
       fw[jj] = e4m3x2_to_f16(*reinterpret_cast<const uint16_t*>(&sb[kBMT + wn * TN + jj][lane * 8 + 2 * j]));
-    }
+    // the codes are read one matrix step at a time (a dword per tile), so
+    // only that step's are held in registers
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      uint32_t ca[TM], cw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ca[i] = *reinterpret_cast<const uint32_t*>(&cb[wm * TM + i][lane * 16 + 4 * kk]);
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj)
+        cw[jj] = *reinterpret_cast<const uint32_t*>(&cb[kBMT + wn * TN + jj][lane * 16 + 4 * kk]);
       f16x8_t wd[TN];
 #pragma unroll
-      for (int jj = 0; jj < TN; ++jj) wd[jj] = dq8_e2m1_f16(vw[jj][kk], fw[jj][kk >> 1]);
+      for (int jj = 0; jj < TN; ++jj) wd[jj] = dq8_e2m1_f16(cw[jj], fw[jj][kk >> 1]);
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const f16x8_t ad = dq8_e2m1_f16(va[i][kk], fa[i][kk >> 1]);
+        const f16x8_t ad = dq8_e2m1_f16(ca[i], fa[i][kk >> 1]);
 #pragma unroll
         for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mma_f16(ad, wd[jj], acc[i][jj]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -378,7 +383,7 @@ hipError_t launch_gemm_w4a4_nvfp4(int a_layout, int w_layout, const uint8_t* a_c
                                   uint16_t* C, int64_t ldc, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   if (a_layout == kLayoutTiled && w_layout == kLayoutTiled)
-    return run_tiled<4, 2, 4, 4>(a_codes, a_scales, a_gs, M, w_codes, w_scales, w_gs, N, K, C, ldc, stream);
+    return run_tiled<2, 4, 8, 4>(a_codes, a_scales, a_gs, M, w_codes, w_scales, w_gs, N, K, C, ldc, stream);
   const dim3 grid((unsigned)((N + kGWaves * 16 * kNT - 1) / (kGWaves * 16 * kNT)),
                   (unsigned)((M + 16 * kMT - 1) / (16 * kMT)));
 #define Q4_W4A4NV(AL, WL)                                                                         \
