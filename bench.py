@@ -268,8 +268,29 @@ def main():
     qbytes = N * K * 2 + wbytes
     extra["quantize_mxfp4_28672x8192"] = {"us": round(ms * 1e3, 2),
                                           "GBps": round(qbytes / (ms * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(qbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                           "bytes": qbytes}
     del empty
+    # the same weight quantized to the other formats (bytes: bf16 read once
+    # plus codes and scales written; NVFP4 also reads it in its tensor-amax
+    # pass), and dequantized back to bf16 (codes and scales read, bf16 written)
+    extra["quantize_28672x8192_other_formats"] = {}
+    for fmt in ("int4", "nvfp4", "int4_zp"):
+        ef = q4.empty_q4(fmt, N, K, device=dev, layout="tiled")
+        fms = timed(torch, lambda ef=ef: q4.q4_quantize(W, ef), 10, 3)
+        fbytes = N * K * 2 + ef.nbytes
+        extra["quantize_28672x8192_other_formats"][fmt] = {
+            "us": round(fms * 1e3, 2), "GBps": round(fbytes / (fms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes}
+        del ef
+    dq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    dms = timed(torch, lambda: q4.q4_dequant(copies[0], dq), 10, 3)
+    dbytes = wbytes + N * K * 2
+    extra["dequant_mxfp4_28672x8192_bf16"] = {"us": round(dms * 1e3, 2),
+                                              "GBps": round(dbytes / (dms * 1e-3) / 1e9, 1),
+                                              "frac_hbm": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                              "bytes": dbytes}
+    del dq
     only = set(filter(None, args.only.split(",")))
 
     def want(name):

@@ -444,8 +444,86 @@ absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_
 
 __global__ void set_word_kernel(uint32_t* p, uint32_t v) { *p = v; }
 
-// Dequantize: one lane per 8 values; OUT 0 = bf16, 1 = fp32.
+// Dequantize the 8 values at (r, k0); OUT 0 = bf16, 1 = fp32.  Every value
+// is fp32(code * scale as stored), then (bf16 output) rounded to nearest
+// even.  MXFP4 blocks whose E8M0 scale keeps every value in the normal fp32
+// range (bytes 2..252) are converted by v_cvt_scalef32_pk_{bf16,f32}_fp4,
+// which multiplies the E2M1 value by the power of two exactly -- the same
+// bits; other blocks take the plain path.  NVFP4 reads its E2M1 values
+// through the same instruction with scale 1 (exact) before the multiply.
 template <int FMT, int OUT, int LAYOUT>
+__device__ __forceinline__ void dequant8(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                         float gs, int64_t r, int64_t k0, int64_t cols, void* __restrict__ dst,
+                                         int64_t ld) {
+  const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols));
+  const int64_t si = scale_off<FMT, LAYOUT>(r, k0, cols);
+  float v[8];
+  if constexpr (FMT == 0) {
+    const float s = fp16_value(reinterpret_cast<const uint16_t*>(scales)[si]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = ((int)(packed << (28 - 4 * j))) >> 28;  // sign-extend nibble j
+      v[j] = (float)q * s;
+    }
+  } else if constexpr (FMT == 4) {
+    const uint32_t word = reinterpret_cast<const uint32_t*>(scales)[si];
+    const float s = fp16_value(word & 0xFFFFu);
+    const int z = (int)(int8_t)((word >> 16) & 0xFFu);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = ((int)(packed << (28 - 4 * j))) >> 28;
+      v[j] = (float)(q - z) * s;
+    }
+  } else if constexpr (FMT == 1) {
+    const uint32_t e = reinterpret_cast<const uint8_t*>(scales)[si];
+    const float s = e8m0_value(e);
+    if (e >= 2u && e <= 252u) {
+      if constexpr (OUT == 0) {
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 0));
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 1));
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 2));
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 3));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
+      } else {
+        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 0);
+        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 1);
+        const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 2);
+        const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 3);
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
+        o[0] = make_float4(p0[0], p0[1], p1[0], p1[1]);
+        o[1] = make_float4(p2[0], p2[1], p3[0], p3[1]);
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * s;
+  } else {
+    const float eff = e4m3_value(reinterpret_cast<const uint8_t*>(scales)[si]) * gs;
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 3);
+    v[0] = p0[0] * eff; v[1] = p0[1] * eff; v[2] = p1[0] * eff; v[3] = p1[1] * eff;
+    v[4] = p2[0] * eff; v[5] = p2[1] * eff; v[6] = p3[0] * eff; v[7] = p3[1] * eff;
+  }
+  if constexpr (OUT == 0) {
+    uint4 o;
+    o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
+    o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
+  } else {
+    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+// One lane per 8 values over the flattened chunks; IDX32: the chunk count
+// fits 32 bits, so the row comes from a 32-bit division.
+template <int FMT, int OUT, int LAYOUT, bool IDX32>
 __global__ void __launch_bounds__(kThreads)
 dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
                const float* gs_ptr, int64_t rows, int64_t cols, void* __restrict__ dst,
@@ -455,48 +533,8 @@ dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scale
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
   for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
        c += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = c / cpr;
-    const int64_t k0 = (c - r * cpr) * 8;
-    const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols));
-    const int64_t si = scale_off<FMT, LAYOUT>(r, k0, cols);
-    float v[8];
-    if constexpr (FMT == 0) {
-      const float s = fp16_value(reinterpret_cast<const uint16_t*>(scales)[si]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = ((int)(packed << (28 - 4 * j))) >> 28;  // sign-extend nibble j
-        v[j] = (float)q * s;
-      }
-    } else if constexpr (FMT == 4) {
-      const uint32_t word = reinterpret_cast<const uint32_t*>(scales)[si];
-      const float s = fp16_value(word & 0xFFFFu);
-      const int z = (int)(int8_t)((word >> 16) & 0xFFu);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = ((int)(packed << (28 - 4 * j))) >> 28;
-        v[j] = (float)(q - z) * s;
-      }
-    } else if constexpr (FMT == 1) {
-      const float s = e8m0_value(reinterpret_cast<const uint8_t*>(scales)[si]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * s;
-    } else {
-      const float eff = e4m3_value(reinterpret_cast<const uint8_t*>(scales)[si]) * gs;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * eff;
-    }
-    if constexpr (OUT == 0) {
-      uint4 o;
-      o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-      o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
-    } else {
-      float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
-      o[0] = make_float4(v[0], v[1], v[2], v[3]);
-      o[1] = make_float4(v[4], v[5], v[6], v[7]);
-    }
+    const int64_t r = IDX32 ? (int64_t)((uint32_t)c / (uint32_t)cpr) : c / cpr;
+    dequant8<FMT, OUT, LAYOUT>(codes, scales, gs, r, (c - r * cpr) * 8, cols, dst, ld);
   }
 }
 
@@ -572,11 +610,14 @@ hipError_t dequant_layout(int fmt, const uint8_t* codes, const void* scales, con
   const int64_t chunks = rows * (cols >> 3);
   if (!chunks) return hipSuccess;
   const unsigned grid = grid_for(chunks);
-#define Q4_DQ(F, O) dequant_kernel<F, O, LAYOUT><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
+  const bool idx32 = chunks <= 0xFFFFFFFFll;
+#define Q4_DQ(F, O)                                                                                              \
+  if (idx32) dequant_kernel<F, O, LAYOUT, true><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld); \
+  else dequant_kernel<F, O, LAYOUT, false><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
   if (dst_dtype == 0) {
-    if (fmt == 0) Q4_DQ(0, 0); else if (fmt == 1) Q4_DQ(1, 0); else if (fmt == 4) Q4_DQ(4, 0); else Q4_DQ(2, 0);
+    if (fmt == 0) { Q4_DQ(0, 0); } else if (fmt == 1) { Q4_DQ(1, 0); } else if (fmt == 4) { Q4_DQ(4, 0); } else { Q4_DQ(2, 0); }
   } else {
-    if (fmt == 0) Q4_DQ(0, 1); else if (fmt == 1) Q4_DQ(1, 1); else if (fmt == 4) Q4_DQ(4, 1); else Q4_DQ(2, 1);
+    if (fmt == 0) { Q4_DQ(0, 1); } else if (fmt == 1) { Q4_DQ(1, 1); } else if (fmt == 4) { Q4_DQ(4, 1); } else { Q4_DQ(2, 1); }
   }
 #undef Q4_DQ
   return hipGetLastError();
