@@ -415,10 +415,34 @@ __global__ void __launch_bounds__(kThreads)
 absmax_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
               uint32_t* gs_bits) {
   // rows over workgroups, a row's 16-byte chunks over the threads (no
-  // division per element); four independent loads in flight per thread
+  // division per element)
   const int cpr = (int)(cols >> 3);
   float a = 0.0f;
-  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+  // two rows at a time, their eight loads per thread in flight together
+  // (a weight too large for the last-level cache streams from HBM: 28672 x
+  // 8192 measured 4% faster than one row at a time), then the remaining row
+  int64_t r = blockIdx.x;
+  for (; r + (int64_t)gridDim.x < rows; r += 2 * (int64_t)gridDim.x) {
+    const uint16_t* rw[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) rw[q] = src + (r + q * (int64_t)gridDim.x) * ld;
+    int c = threadIdx.x;
+    for (; c + 3 * kThreads < cpr; c += 4 * kThreads) {
+      Chunk8 x[2][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[q][u] = load8(rw[q] + (int64_t)(c + u * kThreads) * 8, true);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a = fmaxf(a, absmax8(x[q][u]));
+    }
+    for (; c < cpr; c += kThreads)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) a = fmaxf(a, absmax8(load8(rw[q] + (int64_t)c * 8, true)));
+  }
+  for (; r < rows; r += gridDim.x) {
     const uint16_t* row = src + r * ld;
     int c = threadIdx.x;
     for (; c + 3 * kThreads < cpr; c += 4 * kThreads) {
