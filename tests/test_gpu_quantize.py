@@ -243,10 +243,32 @@ def test_quantize_deterministic():
 # --------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark uses
 # --------------------------------------------------------------------------
+def check_dequant_sampled(qg, qr, nrows=64, seed=5):
+    """The GPU dequantization of the whole tensor (bf16 and fp32) against the
+    oracle's on sampled rows (the first, the last and random ones), bit for
+    bit."""
+    rows, cols = qr.rows, qr.cols
+    rng = np.random.default_rng(seed)
+    pick = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, nrows - 2)]))
+    ref = oracle.dequant_rows(qr, pick)
+    d16 = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    q4.q4_dequant(qg, d16)
+    got16 = d16[torch.from_numpy(pick).to(DEV)].cpu().float().numpy()
+    del d16
+    exp16 = oracle.bf16_bits_to_f32(oracle.f32_to_bf16_bits(ref))
+    assert np.array_equal(got16.view(np.uint32), exp16.view(np.uint32))
+    d32 = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    q4.q4_dequant(qg, d32)
+    got32 = d32[torch.from_numpy(pick).to(DEV)].cpu().numpy()
+    del d32
+    assert np.array_equal(got32.view(np.uint32), ref.view(np.uint32))
+
+
 def test_full_int4_gemv_weight():
     wl = workloads.int4_gemv()
     qg, qr = quant_both(wl.tensors["W"], "int4")
     assert_quant_equal(qg, qr, "int4")
+    check_dequant_sampled(qg, qr)
 
 
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
@@ -255,6 +277,8 @@ def test_full_mxfp4_decode_weight(layout):
     log("quantize 28672x8192 MXFP4", layout)
     qg, qr = quant_both(wl.tensors["W"], "mxfp4", layout=layout)
     assert_quant_equal(qg, qr, "mxfp4")
+    log("dequantize 28672x8192 MXFP4 (sampled rows)", layout)
+    check_dequant_sampled(qg, qr)
 
 
 @pytest.mark.parametrize("layout", ("rows", "tiled"))
@@ -263,6 +287,8 @@ def test_full_nvfp4_prefill_weight(layout):
     log("quantize 8192x8192 NVFP4", layout)
     qg, qr = quant_both(wl.tensors["W"], "nvfp4", layout=layout)
     assert_quant_equal(qg, qr, "nvfp4")
+    log("dequantize 8192x8192 NVFP4 (sampled rows)", layout)
+    check_dequant_sampled(qg, qr)
 
 
 def test_full_w4a4_operands():
