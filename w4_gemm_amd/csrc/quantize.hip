@@ -74,8 +74,9 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const Chunk8& c, float scale) {
 // that is monotone in the value.  Here the quotient is formed as a product
 // with a reciprocal, twice, the product nudged down and up by a relative
 // 2^-20: the reciprocal (v_rcp_f32, within 1 ulp; an fp32 division, within
-// 1/2 ulp) and the products add under 2^-21 relative error in all, so the
-// two nudged products bracket the correctly rounded quotient.  Where both
+// 1/2 ulp) and the products add under 2^-21 relative error in all, and the
+// fp32 quotient itself is within 2^-23 of the exact one (two roundings for
+// the block scale), so the two nudged products bracket it.  Where both
 // round to the same code, so does the quotient; where they differ (a
 // quotient within about 2^-20 of a rounding boundary, an exact tie) the
 // division is done.  This needs the operands in the normal range: the
