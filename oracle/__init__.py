@@ -157,8 +157,11 @@ def nv_block_scale_code(amax_b: float, gs: float) -> int:
 
 
 def set_ties_toward_zero(on: bool) -> None:
-    """Test-only switch: exact E2M1/E4M3/FP16/INT ties go to the lower
-    neighbour (the formats.py argmin behaviour) instead of the even code."""
+    """Test-only switch: exact E2M1 ties go to the lower neighbour (what the
+    argmin of formats.py fp4() returns, "Quantization in deployment", Fake
+    quantization) instead of the even code.  E4M3, fp16 and INT4 roundings
+    keep ties to even either way, as formats.py's float8_e4m3fn cast and
+    fake_int4's torch.round do."""
     lib().oracle_set_ties_toward_zero(1 if on else 0)
 
 

@@ -30,8 +30,9 @@
  *   - every rounding to a narrow format is round-to-nearest, ties to the
  *     code whose last bit is even (the chains page checks its examples with
  *     a round-to-nearest-even library; fake_int4 uses torch.round, which is
- *     half-to-even).  The formats.py argmin would send exact ties toward
- *     zero; set_ties_toward_zero(1) reproduces that, for tests only;
+ *     half-to-even).  The formats.py fp4() argmin would send exact E2M1
+ *     ties toward zero; set_ties_toward_zero(1) reproduces that in the E2M1
+ *     encoder only, for tests (formats.py's E4M3 cast keeps ties to even);
  *   - the element is divided by the scale as stored (fp16 for INT4, 2^e for
  *     MXFP4, fp32(E4M3 * global) for NVFP4), as nvfp4() does;
  *   - an INT4 block whose fp16 scale is 0, and an NVFP4 block whose E4M3
@@ -89,9 +90,11 @@ static int g_ties_toward_zero = 0;
 void oracle_set_ties_toward_zero(int on) { g_ties_toward_zero = on ? 1 : 0; }
 
 /* Nearest entry of an increasing table to v (v >= table[0]); on an exact
- * tie between two neighbours, the even code (or, with the test-only switch,
- * the lower one).  Distances are computed in double, where they are exact
- * for every fp32 v and every table value used here. */
+ * tie between two neighbours, the even code.  Distances are computed in
+ * double, where they are exact for every fp32 v and every table value used
+ * here.  (The test-only tie switch does not reach this search: formats.py
+ * rounds E4M3 with torch's float8_e4m3fn cast, which is round-to-nearest
+ * with ties to even; only its fp4() rounds by an argmin.) */
 static int nearest_code(double v, double (*value)(int), int ncodes)
 {
     int lo = 0, hi = ncodes - 1;
@@ -111,8 +114,6 @@ static int nearest_code(double v, double (*value)(int), int ncodes)
         return lo;
     if (dhi < dlo)
         return hi;
-    if (g_ties_toward_zero)
-        return lo;
     return (lo % 2 == 0) ? lo : hi;
 }
 

@@ -249,8 +249,9 @@ def test_block_max_5_mxfp4_vs_nvfp4():
 
 
 def test_mx_power_of_two_scale_leaves_max_in_4_to_8():
-    """The page: a power-of-two scale leaves a block's largest value anywhere
-    in [4, 8) of the scaled range."""
+    """MXFP4's scale 2^(floor(log2 amax) - 2) divides a block's maximum down
+    to some value in [4, 8), never more than a factor two from the top of
+    the E2M1 range ("Quantization chains", "MXFP4 against NVFP4 scales")."""
     rng = np.random.default_rng(4)
     amax = (rng.random(20000) * 2.0 ** rng.integers(-20, 20, 20000)).astype(np.float32) + 1e-9
     for a in amax[:5000]:
