@@ -223,6 +223,24 @@ def test_strided_operands_match_contiguous(fmt, layout):
     q4.q4_grouped_gemm(a_s, ga, of, qg, N, g1[:, :N])
     torch.cuda.synchronize()
     assert torch.equal(g0, g1[:, :N]) and torch.isnan(g1[:, N:]).all()
+    # odd leading dimensions, and outputs that start at an odd element (2-byte
+    # but not 4-byte aligned): the kernels' 4-wide bf16 stores fall back to
+    # narrower ones and the results are the same
+    for off, extra in ((0, 1), (1, 3)):
+        log("strided", fmt, layout, "output offset", off, "ld", N + off + extra)
+        c2 = torch.full((40, N + off + extra), float("nan"), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemm(a, qn, c2[:, off:off + N])
+        g2 = torch.full((P, N + off + extra), float("nan"), dtype=torch.bfloat16, device=DEV)
+        q4.q4_grouped_gemm(a, ga, of, qg, N, g2[:, off:off + N])
+        y2 = torch.full((16, N + off + extra), float("nan"), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemv(qn, a[:16].contiguous(), y2[:, off:off + N])
+        torch.cuda.synchronize()
+        y0 = torch.empty((16, N), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemv(qn, a[:16].contiguous(), y0)
+        torch.cuda.synchronize()
+        for got, ref in ((c2, c0), (g2, g0), (y2, y0)):
+            assert torch.equal(got[:, off:off + N], ref)
+            assert torch.isnan(got[:, :off]).all() and torch.isnan(got[:, off + N:]).all()
 
 
 # --------------------------------------------------------------------------

@@ -118,6 +118,59 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+def _on_gpu(*args):
+    """Every tensor argument (or Q4Tensor buffer) is on the GPU.  Checked
+    after the shapes, so that the shape checks can be tested on the CPU."""
+    for name, t in args:
+        if t is None:
+            continue
+        ts = ((f"{name}.codes", t.codes), (f"{name}.scales", t.scales),
+              (f"{name}.global_scale", t.global_scale)) if isinstance(t, Q4Tensor) else ((name, t),)
+        for n, x in ts:
+            if x is not None and x.device.type != "cuda":
+                raise ValueError(f"{n} must be a GPU tensor (got device {x.device})")
+
+
+def _matrix(t: torch.Tensor, name: str, dtype, rows: int, cols: int, exact_cols: bool = False):
+    """A 2-D argument with unit column stride, at least `rows` x `cols`
+    (exactly `cols` columns if exact_cols).  Checked before any library
+    call, so a wrong tensor never reaches a kernel as a pointer."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D (got shape {tuple(t.shape)})")
+    if exact_cols and t.shape[1] != cols:
+        raise ValueError(f"{name} must have {cols} columns (got {t.shape[1]})")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} must be at least {rows} x {cols} (got {tuple(t.shape)})")
+    if t.numel() and (t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) < t.shape[1])):
+        raise ValueError(f"{name} must have unit column stride and non-overlapping rows")
+
+
+def _vector(t: torch.Tensor, name: str, dtype, n: int):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise ValueError(f"{name} must be a {dtype} tensor")
+    if not t.is_contiguous() or t.numel() < n:
+        raise ValueError(f"{name} must be contiguous with at least {n} entries (got {t.numel()})")
+
+
+def _q4(q: "Q4Tensor", name: str):
+    """A quantized tensor's buffers: contiguous, as large as q4_sizes says
+    for its format, layout and shape."""
+    if not isinstance(q, Q4Tensor):
+        raise ValueError(f"{name} must be a Q4Tensor")
+    cb, sb = q4_sizes(q.fmt, q.rows, q.cols, q.layout)
+    for part, t, need in (("codes", q.codes, cb), ("scales", q.scales, sb)):
+        if not t.is_contiguous() or t.numel() * t.element_size() < need:
+            raise ValueError(f"{name}.{part} must be contiguous and hold {need} bytes")
+    if q.fmt == NVFP4:
+        if q.global_scale is None:
+            raise ValueError(f"{name}.global_scale is required for NVFP4")
+        _vector(q.global_scale, f"{name}.global_scale", torch.float32, 1)
+
+
 def _fmt(fmt) -> int:
     return FORMAT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
 
@@ -201,8 +254,11 @@ def empty_q4(fmt, rows: int, cols: int, device="cuda", layout=LAYOUT_ROWS) -> Q4
 def q4_quantize(src: torch.Tensor, dst: Q4Tensor, nv_global_in: Optional[torch.Tensor] = None,
                 stream=None) -> Q4Tensor:
     """Quantize bf16 src [rows, >= cols] (row stride src.stride(0)) into dst."""
-    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.stride(1) != 1:
-        raise ValueError("src must be a 2-D bf16 tensor with unit column stride")
+    _matrix(src, "src", torch.bfloat16, dst.rows, dst.cols)
+    _q4(dst, "dst")
+    if nv_global_in is not None:
+        _vector(nv_global_in, "nv_global_in", torch.float32, 1)
+    _on_gpu(("src", src), ("dst", dst), ("nv_global_in", nv_global_in))
     desc = dst.c()
     _check(lib().q4_quantize(_ptr(src), src.stride(0), ctypes.byref(desc), _ptr(nv_global_in),
                              _stream(stream)), "q4_quantize")
@@ -224,8 +280,9 @@ def q4_dequant(src: Q4Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
         dt = 1
     else:
         raise ValueError("dst must be bf16 or float32")
-    if dst.dim() != 2 or dst.stride(1) != 1:
-        raise ValueError("dst must be 2-D with unit column stride")
+    _matrix(dst, "dst", dst.dtype, src.rows, src.cols)
+    _q4(src, "src")
+    _on_gpu(("src", src), ("dst", dst))
     desc = src.c()
     _check(lib().q4_dequant(ctypes.byref(desc), _ptr(dst), dt, dst.stride(0), _stream(stream)),
            "q4_dequant")
@@ -234,6 +291,10 @@ def q4_dequant(src: Q4Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
 
 def q4_gemv(W: Q4Tensor, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
     """y[b, n] = sum_k x[b, k] w'[n, k] for b < x.shape[0] (<= 16)."""
+    _q4(W, "W")
+    _matrix(x, "x", torch.bfloat16, 0, W.cols, exact_cols=True)
+    _matrix(y, "y", torch.bfloat16, x.shape[0], W.rows)
+    _on_gpu(("W", W), ("x", x), ("y", y))
     desc = W.c()
     _check(lib().q4_gemv(ctypes.byref(desc), _ptr(x), x.shape[0], x.stride(0), _ptr(y),
                          y.stride(0), _stream(stream)), "q4_gemv")
@@ -244,6 +305,17 @@ def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
     """C = A' W'^T.  A is a bf16 tensor [M, K] (W4A16), an MXFP4 or NVFP4
     Q4Tensor (W4A4, with W in the same format) or an FP8_ROW Q4Tensor (W4A8,
     with W INT4)."""
+    _q4(W, "W")
+    if isinstance(A, Q4Tensor):
+        _q4(A, "A")
+        if A.cols != W.cols:
+            raise ValueError(f"A has {A.cols} columns, W {W.cols}")
+        M = A.rows
+    else:
+        _matrix(A, "A", torch.bfloat16, 0, W.cols, exact_cols=True)
+        M = A.shape[0]
+    _matrix(C, "C", torch.bfloat16, M, W.rows)
+    _on_gpu(("W", W), ("A", A), ("C", C))
     wd = W.c()
     if isinstance(A, Q4Tensor):
         ad = A.c()
@@ -261,10 +333,17 @@ def q4_grouped_gemm(A: torch.Tensor, gather: torch.Tensor, offsets: torch.Tensor
     """For expert e, rows p in [offsets[e], offsets[e+1]):
     C[p] = A[gather[p]] . w'_e^T, with W stacked expert-major (E*N rows).
     gather None: row p reads A[p] (P = C.shape[0] rows)."""
-    if (gather is not None and gather.dtype != torch.int32) or offsets.dtype != torch.int32:
-        raise ValueError("gather and offsets must be int32")
+    _q4(W, "W")
+    _matrix(A, "A", torch.bfloat16, 0, W.cols, exact_cols=True)
+    _vector(offsets, "offsets", torch.int32, 1)
     E = offsets.numel() - 1
+    if W.rows != E * N:
+        raise ValueError(f"W has {W.rows} rows, not experts ({E}) x N ({N})")
+    if gather is not None:
+        _vector(gather, "gather", torch.int32, 0)
     P = C.shape[0] if gather is None else gather.numel()
+    _matrix(C, "C", torch.bfloat16, P, N)
+    _on_gpu(("W", W), ("A", A), ("gather", gather), ("offsets", offsets), ("C", C))
     wd = W.c()
     _check(lib().q4_grouped_gemm(_ptr(A), A.stride(0), A.shape[0], _ptr(gather), _ptr(offsets),
                                  E, P, ctypes.byref(wd), N, _ptr(C), C.stride(0),
@@ -285,8 +364,8 @@ class Routing:
 def q4_moe_route(logits: torch.Tensor, k: int, stream=None) -> Routing:
     """Top-k routing with softmax gates and the expert-major dispatch order
     for fp32 router logits [T, E] (unit column stride)."""
-    if logits.dtype != torch.float32 or logits.dim() != 2 or (logits.numel() and logits.stride(1) != 1):
-        raise ValueError("logits must be a 2-D float32 tensor with unit column stride")
+    _matrix(logits, "logits", torch.float32, 0, 0)
+    _on_gpu(("logits", logits))
     T, E = logits.shape
     dev = logits.device
     r = Routing(torch.empty((T, k), dtype=torch.int32, device=dev),
@@ -302,9 +381,12 @@ def q4_moe_route(logits: torch.Tensor, k: int, stream=None) -> Routing:
 
 def q4_swiglu(gu: torch.Tensor, inter: int, h: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """h = silu(gu[:, :inter]) * gu[:, inter:2*inter] (bf16)."""
+    _matrix(gu, "gu", torch.bfloat16, 0, 2 * inter)
     P = gu.shape[0]
     if h is None:
         h = torch.empty((P, inter), dtype=torch.bfloat16, device=gu.device)
+    _matrix(h, "h", torch.bfloat16, P, inter)
+    _on_gpu(("gu", gu), ("h", h))
     _check(lib().q4_swiglu(_ptr(gu), gu.stride(0), P, inter, _ptr(h), h.stride(0), _stream(stream)),
            "q4_swiglu")
     return h
@@ -314,9 +396,14 @@ def q4_moe_combine(y: torch.Tensor, r: Routing, out: Optional[torch.Tensor] = No
                    stream=None) -> torch.Tensor:
     """out[t] = sum_j r.weights[t, j] * y[r.inv[t, j]] (bf16)."""
     T, k = r.inv.shape
+    _vector(r.inv, "r.inv", torch.int32, T * k)
+    _vector(r.weights, "r.weights", torch.float32, T * k)
+    _matrix(y, "y", torch.bfloat16, T * k, 0)
     N = y.shape[1]
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
+    _matrix(out, "out", torch.bfloat16, T, N)
+    _on_gpu(("y", y), ("r.inv", r.inv), ("r.weights", r.weights), ("out", out))
     _check(lib().q4_moe_combine(_ptr(y), y.stride(0), _ptr(r.inv), _ptr(r.weights), T, k, N, _ptr(out),
                                 out.stride(0), _stream(stream)), "q4_moe_combine")
     return out
@@ -327,10 +414,17 @@ def q4_grouped_gemm_swiglu(A: torch.Tensor, gather: Optional[torch.Tensor], offs
     """H[p] = silu(A[gather[p]] . W_gate_e^T) * (A[gather[p]] . W_up_e^T),
     with W's 2*inter rows per expert alternating 16-row gate and up tiles
     (see interleave_gate_up); gather None: row p reads A[p]."""
-    if (gather is not None and gather.dtype != torch.int32) or offsets.dtype != torch.int32:
-        raise ValueError("gather and offsets must be int32")
+    _q4(W, "W")
+    _matrix(A, "A", torch.bfloat16, 0, W.cols, exact_cols=True)
+    _vector(offsets, "offsets", torch.int32, 1)
     E = offsets.numel() - 1
+    if W.rows != E * 2 * inter:
+        raise ValueError(f"W has {W.rows} rows, not experts ({E}) x 2 x inter ({inter})")
+    if gather is not None:
+        _vector(gather, "gather", torch.int32, 0)
     P = H.shape[0] if gather is None else gather.numel()
+    _matrix(H, "H", torch.bfloat16, P, inter)
+    _on_gpu(("W", W), ("A", A), ("gather", gather), ("offsets", offsets), ("H", H))
     wd = W.c()
     _check(lib().q4_grouped_gemm_swiglu(_ptr(A), A.stride(0), A.shape[0], _ptr(gather), _ptr(offsets), E, P,
                                         ctypes.byref(wd), inter, _ptr(H), H.stride(0), _stream(stream)),

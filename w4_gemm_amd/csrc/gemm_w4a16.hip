@@ -256,7 +256,7 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
         const int n = n0 + 16 * jj;
         const f32x4_t v = acc[r][jj];
         if (n + 3 < N) {
-          *reinterpret_cast<uint2*>(crow + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+          store_bf16x4(crow + n, v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)

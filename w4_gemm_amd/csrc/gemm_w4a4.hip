@@ -23,11 +23,14 @@
 //     three buffers.  Scales are copied per group of four stages (16 x 256 B for
 //     each operand) into two buffers.  Every fragment read from LDS is one
 //     contiguous kilobyte (conflict-free).
-//   * one barrier per stage: each wave first waits (explicit vmcnt) for its
-//     own copies of the current stage, the barrier then makes every wave's
-//     copies visible and also guarantees that the buffer the next copies
-//     overwrite is no longer read.  The stage loop is unrolled by four so
-//     each wait count is a constant.
+//   * one barrier per stage: each wave first waits for its own copies of
+//     the current stage (explicit vmcnt) and for every LDS read it has
+//     issued (lgkmcnt 0), so the fragments of the previous stage are in
+//     registers; the barrier then makes every wave's copies visible, and
+//     the buffer the next copies overwrite -- the previous stage's -- is no
+//     longer read by any wave, whatever the compiler does with the matrix
+//     instructions that consume those registers.  The stage loop is
+//     unrolled by four so each wait count is a constant.
 //   * workgroups are ordered so that the 32 running on one XCD cover a
 //     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
 #include "q4_launch.h"
@@ -155,23 +158,23 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
   // The tiled layout has K % 512 == 0, so S is a multiple of 4.
   for (int s0 = 0; s0 < S; s0 += 4) {
     // j = 0
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier_loose();
     issue_codes(s0 + 2);
     compute(s0, 0);
     // j = 1
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier_loose();
     issue_codes(s0 + 3);
     compute(s0 + 1, 1);
     // j = 2: group s0+4 starts a new scale group
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier_loose();
     issue_codes(s0 + 4);
     issue_scales(s0 + 4);
     compute(s0 + 2, 2);
     // j = 3: group s0+4 (outstanding) also holds its scale copy
-    wait_vmcnt<kCopies + 1>();
+    wait_vmcnt_lgkm0<kCopies + 1>();
     stage_barrier_loose();
     issue_codes(s0 + 5);
     compute(s0 + 3, 3);

@@ -223,8 +223,9 @@ w4a4nv_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
   issue_scales(0);
   issue_codes(1);
 
-  // iteration s: wait for stage s (stage s+1 may stay in flight), barrier,
-  // issue stage s+2 into the buffers of stage s-1, compute stage s.  Copies
+  // iteration s: wait for stage s (stage s+1 may stay in flight) and for
+  // this wave's LDS reads of stage s-1, barrier, issue stage s+2 into the
+  // buffers of stage s-1 (no wave reads them any more), compute stage s.  Copies
   // of stage s+1: kCopies, plus kScaleCopies when (s+1) % 4 == 0.  The tiled
   // layout has K % 512 == 0, so S is a multiple of 4.
   using J0 = std::integral_constant<int, 0>;
@@ -232,20 +233,20 @@ w4a4nv_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restri
   using J2 = std::integral_constant<int, 2>;
   using J3 = std::integral_constant<int, 3>;
   for (int s0 = 0; s0 < S; s0 += 4) {
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 2);
     compute(s0, J0());
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 3);
     compute(s0 + 1, J1());
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 4);
     issue_scales(s0 + 4);
     compute(s0 + 2, J2());
-    wait_vmcnt<kCopies + kScaleCopies>();
+    wait_vmcnt_lgkm0<kCopies + kScaleCopies>();
     stage_barrier();
     issue_codes(s0 + 5);
     compute(s0 + 3, J3());

@@ -27,8 +27,10 @@
 //     (6 per wave per stage), two stages ahead, into three buffers; the W
 //     group scales of four stages (16 x 128 B) are copied once per group of
 //     four into two buffers;
-//   * one barrier per stage, explicit vmcnt waits, the stage loop unrolled
-//     by four (the scheme of the W4A4 kernel in gemm_w4a4.hip);
+//   * one barrier per stage, before it a wait for this wave's copies of the
+//     stage (explicit vmcnt) and for all its LDS reads (lgkmcnt 0), so no
+//     wave still reads the buffer the next copies overwrite; the stage loop
+//     unrolled by four (the scheme of the W4A4 kernel in gemm_w4a4.hip);
 //   * workgroups ordered so the 32 running on one XCD share A and W panels.
 // Generic kernel (any layout): one thread per output, the same promotion
 // order, for the shapes and layouts the tiled kernel does not take.
@@ -197,23 +199,24 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
   issue_scales(0);
   issue_codes(1);
   // iteration s: wait for copy group s (group s+1 may stay in flight: its
-  // kCopies code copies, plus its scale copy when (s+1) % 4 == 0), barrier,
-  // issue group s+2 into the buffers of stage s-1, compute stage s.
+  // kCopies code copies, plus its scale copy when (s+1) % 4 == 0) and for
+  // this wave's LDS reads of stage s-1, barrier, issue group s+2 into the
+  // buffers of stage s-1, compute stage s.
   for (int s0 = 0; s0 < S; s0 += 4) {
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 2);
     compute(s0, 0);
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 3);
     compute(s0 + 1, 1);
-    wait_vmcnt<kCopies>();
+    wait_vmcnt_lgkm0<kCopies>();
     stage_barrier();
     issue_codes(s0 + 4);
     issue_scales(s0 + 4);
     compute(s0 + 2, 2);
-    wait_vmcnt<kCopies + 1>();
+    wait_vmcnt_lgkm0<kCopies + 1>();
     stage_barrier();
     issue_codes(s0 + 5);
     compute(s0 + 3, 3);

@@ -270,7 +270,7 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
                 v[q] = z / (1.0f + expf(-z)) * acc[1][bt][q];
               }
             }
-            *reinterpret_cast<uint2*>(C + (int64_t)p * ldc + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+            store_bf16x4(C + (int64_t)p * ldc + n, v[0], v[1], v[2], v[3]);
           }
         }
       }
@@ -285,7 +285,7 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
           if (bt < nb && p < r1) {
             const int g = gather ? gather[p] : p;
             const f32x4_t v = (g >= 0 && g < T) ? acc[t][bt] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            *reinterpret_cast<uint2*>(C + (int64_t)p * ldc + n) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+            store_bf16x4(C + (int64_t)p * ldc + n, v[0], v[1], v[2], v[3]);
           }
         }
       }

@@ -40,6 +40,26 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return as_u32(__builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Four consecutive bf16 outputs: one 8-byte store where dst is 8-byte
+// aligned (the usual case: C 16-byte aligned, ldc a multiple of 4), else
+// two 4-byte or four 2-byte stores -- the C ABI accepts any 2-byte
+// aligned output and any leading dimension.
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, float v0, float v1, float v2, float v3) {
+  const uint32_t lo = pk_bf16(v0, v1), hi = pk_bf16(v2, v3);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(dst);
+  if ((a & 7) == 0) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  } else if ((a & 3) == 0) {
+    reinterpret_cast<uint32_t*>(dst)[0] = lo;
+    reinterpret_cast<uint32_t*>(dst)[1] = hi;
+  } else {
+    dst[0] = (uint16_t)lo;
+    dst[1] = (uint16_t)(lo >> 16);
+    dst[2] = (uint16_t)hi;
+    dst[3] = (uint16_t)(hi >> 16);
+  }
+}
+
 // 8 E2M1 codes times an arbitrary fp32 scale (NVFP4: E4M3 * gs) -> 8 bf16:
 // exact fp32 code values, one fp32 multiply, one rounding to bf16.
 __device__ __forceinline__ bf16x8_t dq8_e2m1_mul(uint32_t w, float scale) {
