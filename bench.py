@@ -278,10 +278,14 @@ def main():
     for fmt in ("int4", "nvfp4", "int4_zp"):
         ef = q4.empty_q4(fmt, N, K, device=dev, layout="tiled")
         fms = timed(torch, lambda ef=ef: q4.q4_quantize(W, ef), 10, 3)
-        fbytes = N * K * 2 + ef.nbytes
+        # NVFP4 reads the bf16 weight twice: the tensor-amax pass, then the
+        # block pass (which needs the tensor scale first)
+        reads = 2 if fmt == "nvfp4" else 1
+        fbytes = reads * N * K * 2 + ef.nbytes
         extra["quantize_28672x8192_other_formats"][fmt] = {
             "us": round(fms * 1e3, 2), "GBps": round(fbytes / (fms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes}
+            "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes,
+            "weight_reads": reads}
         del ef
     dq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     dms = timed(torch, lambda: q4.q4_dequant(copies[0], dq), 10, 3)
@@ -475,10 +479,28 @@ def bench_w4a4(torch, q4, workloads, dev, seed, fmt="mxfp4"):
     ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     peak = ("frac_fp4_peak", FP4_PEAK_TFLOPS) if fmt == "mxfp4" else ("frac_fp16_peak", FP16_PEAK_TFLOPS)
-    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
-            peak[0]: round(tflops / peak[1], 4),
-            "act_quantize_us": round(ams * 1e3, 1),
-            "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+    res = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+           peak[0]: round(tflops / peak[1], 4),
+           "act_quantize_us": round(ams * 1e3, 1),
+           "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+    if fmt == "mxfp4":
+        # one layer of a W4A4 chain: the GEMM's output is the next layer's A.
+        # Unfused: bf16 C, then a separate q4_quantize pass over it; fused:
+        # the GEMM's epilogue writes C as MXFP4 codes + E8M0 scales directly
+        # (q4_gemm_quantized), so the next GEMM starts from 4-bit activations
+        qc = q4.empty_q4("mxfp4", M, N, device=dev, layout="tiled")
+
+        def unfused():
+            q4.q4_gemm(qa, qw, C)
+            q4.q4_quantize(C, qc)
+
+        ums = timed(torch, unfused, 10, 2)
+        fms = timed(torch, lambda: q4.q4_gemm_quantized(qa, qw, qc), 10, 2)
+        res["layer_with_separate_act_quantize_us"] = round(ums * 1e3, 1)
+        res["layer_with_fused_act_quantize_us"] = round(fms * 1e3, 1)
+        res["fused_epilogue_saves_us"] = round((ums - fms) * 1e3, 1)
+        res["fused_TFLOPs"] = round(2.0 * M * N * K / (fms * 1e-3) / 1e12, 1)
+    return res
 
 
 def bench_w4a8(torch, q4, workloads, dev, seed):
@@ -500,11 +522,26 @@ def bench_w4a8(torch, q4, workloads, dev, seed):
             "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wl, wbytes, batches):
     """The oracle, as it stands, on the headline workload: for each batch it
-    dequantizes the MXFP4 weight (plain C) and takes the fp64 product
-    (numpy).  Repeated until about 10 s of CPU work."""
+    dequantizes the MXFP4 weight (plain C, OpenMP over rows) and takes the
+    fp64 product (numpy).  Timed with every host thread the process may use
+    (repeated until about 10 s of work) and with one thread (OpenMP and the
+    BLAS capped at 1 by threadpoolctl; one step)."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
 
@@ -513,19 +550,32 @@ def cpu_baseline(wl, wbytes, batches):
     qr = oracle.quantize("mxfp4", w)
     del w
     xs = {b: wl.tensors[f"x{b}"].float().numpy() for b in batches}
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        for b in batches:
-            oracle.gemv(qr, xs[b])
-        steps += 1
-        el = time.perf_counter() - t0
-        if el > 10.0 or steps >= 5:
-            break
-    per_step = el / steps
-    return {"value": round(len(batches) * wbytes / per_step / 1e9, 3), "unit": "GB/s",
-            "cores": cpu_cores(), "kind": "oracle",
-            "sample": f"full workload: 28672x8192 MXFP4 weight, B={list(batches)}, {steps} step(s), "
-                      f"{per_step:.2f} s/step"}
+
+    def run(seconds, max_steps):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            for b in batches:
+                oracle.gemv(qr, xs[b])
+            steps += 1
+            el = time.perf_counter() - t0
+            if el > seconds or steps >= max_steps:
+                return el / steps, steps
+
+    log("cpu baseline: all threads")
+    per_step, steps = run(10.0, 5)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [cpu_cores()])
+    log("cpu baseline: one thread")
+    with threadpool_limits(limits=1):
+        per_step_1, steps_1 = run(20.0, 1)
+    gbs = len(batches) * wbytes / per_step / 1e9
+    gbs_1 = len(batches) * wbytes / per_step_1 / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"full workload: 28672x8192 MXFP4 weight, B={list(batches)}, {steps} step(s) on "
+                      f"{threads} threads ({per_step:.2f} s/step), {steps_1} on one thread "
+                      f"({per_step_1:.2f} s/step)",
+            "single_thread_GBps": round(gbs_1, 4), "single_thread_s_per_step": round(per_step_1, 3),
+            "all_threads_s_per_step": round(per_step, 3),
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": cpu_cores()}
 
 
 if __name__ == "__main__":

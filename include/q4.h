@@ -228,6 +228,31 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
                   const q4_tensor* W, void* C_bf16, int64_t ldc, void* stream);
 
 /*
+ * The GEMM of q4_gemm with its output written quantized by the kernel's
+ * epilogue: C_q receives exactly the codes and scales that q4_quantize(C_q)
+ * writes for the bf16 C that q4_gemm writes (each fp32 sum rounded to bf16,
+ * then block-quantized), and C is never written in bf16 nor read back.  This
+ * is the activation quantization of the next W4A4 layer done at the end of
+ * the kernel that produces the activations, which saves a pass that reads
+ * and writes them ("Quantization in deployment", Exercises, "The cost of
+ * block FP8": activation scales computed at the end of the previous kernel).
+ *   C_q  MXFP4, or NVFP4 with the tensor scale taken from nv_global_in
+ *        (device fp32[1]; required for NVFP4 and NULL otherwise; its value
+ *        is also written to C_q->global_scale: an epilogue cannot wait for
+ *        the amax of the whole output, so the scale is the caller's, e.g.
+ *        a calibrated one).  C_q->rows == M, C_q->cols == N == W->rows,
+ *        N % 32 == 0; either layout (tiled: N % 512 == 0, padding rows
+ *        written as the quantization of zeros).
+ *   Operands: A_bf16 [M][lda] with W of any weight format in the tiled
+ *        layout (W4A16), or A_q MXFP4 tiled with W MXFP4 tiled (W4A4).
+ *        Other combinations: Q4_ERR_FORMAT.
+ * M == 0 or N == 0 is a no-op.  C_q must not alias the operands.
+ */
+q4_status q4_gemm_quantized(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A_q,
+                            const q4_tensor* W, const q4_tensor* C_q, const float* nv_global_in,
+                            void* stream);
+
+/*
  * Grouped per-expert GEMM for MoE ("Low-bit inference for very large MoE",
  * "A few details": one low-bit weight matrix per expert, rows grouped by
  * routing).  W holds E experts stacked expert-major: W->rows == E*N, expert

@@ -215,3 +215,34 @@ def test_moe_validation():
     assert L.q4_moe_combine(B, 64, B, B, 4, 0, 64, B, 64, None) == SHAPE
     assert L.q4_moe_combine(B, 64, None, B, 4, 2, 64, B, 64, None) == NULL
     assert L.q4_moe_combine(B, 64, B, B, 0, 2, 64, B, 64, None) == OK
+
+
+def test_gemm_quantized_validation():
+    L = q4.lib()
+    T = q4.LAYOUT_TILED
+    w = desc(rows=512, cols=512, layout=T)
+    wmx = desc(rows=512, cols=512, layout=T)
+    a = desc(rows=64, cols=512, layout=T)
+    c = desc(rows=64, cols=512)                                   # MXFP4 output, row-major
+    cn = desc(fmt=q4.NVFP4, rows=64, cols=512, gs=A16)            # NVFP4 output
+    R = lambda *x: L.q4_gemm_quantized(*x, None)                  # noqa: E731
+    by = ctypes.byref
+    assert R(64, A16, 512, None, by(w), None, None) == NULL
+    assert R(64, A16, 512, None, by(w), by(cn), None) == NULL                # NVFP4 needs a tensor scale
+    assert R(64, A16, 512, None, by(w), by(c), A16) == FMT                   # only NVFP4 takes one
+    assert R(64, A16, 512, None, by(w), by(cn), A_ODD) == ALIGN
+    assert R(64, A16, 512, None, by(desc(rows=512, cols=512)), by(c), None) == FMT   # W must be tiled
+    assert R(64, A16, 512, None, by(w), by(desc(fmt=q4.INT4_G128, rows=64, cols=512)), None) == FMT
+    assert R(64, A16, 512, by(a), by(w), by(c), None) == FMT                 # both operands given
+    assert R(64, None, 0, None, by(w), by(c), None) == NULL
+    assert R(64, None, 0, by(desc(rows=64, cols=512)), by(wmx), by(c), None) == FMT    # A must be tiled
+    assert R(64, None, 0, by(desc(fmt=q4.NVFP4, rows=64, cols=512, gs=A16, layout=T)),
+             by(desc(fmt=q4.NVFP4, rows=512, cols=512, gs=A16, layout=T)), by(c), None) == FMT
+    assert R(32, A16, 512, None, by(w), by(c), None) == SHAPE                # C rows != M
+    assert R(64, A16, 512, None, by(w), by(desc(rows=64, cols=256)), None) == SHAPE
+    assert R(64, A16, 512, None, by(desc(rows=48, cols=512, layout=T)),
+             by(desc(fmt=q4.NVFP4, rows=64, cols=48, gs=A16)), A16) == SHAPE   # N % 32
+    assert R(64, A16, 500, None, by(w), by(c), None) == SHAPE                # lda < K
+    assert R(64, A_ODD, 512, None, by(w), by(c), None) == ALIGN
+    assert R(32, None, 0, by(a), by(wmx), by(c), None) == SHAPE              # A rows != M
+    assert R(0, A16, 512, None, by(w), by(desc(rows=0, cols=512)), None) == OK

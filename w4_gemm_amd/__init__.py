@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "INT4_ZP", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
-    "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm",
+    "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
     "moe_layer", "interleave_gate_up",
     "empty_q4", "quantize", "LIB_PATH",
@@ -80,6 +80,7 @@ def _lib_handle():
             "q4_dequant": ([P, vp, ctypes.c_int, i64, vp], ctypes.c_int),
             "q4_gemv": ([P, vp, i64, i64, vp, i64, vp], ctypes.c_int),
             "q4_gemm": ([i64, vp, i64, P, P, vp, i64, vp], ctypes.c_int),
+            "q4_gemm_quantized": ([i64, vp, i64, P, P, P, vp, vp], ctypes.c_int),
             "q4_grouped_gemm": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
                                 ctypes.c_int),
             "q4_grouped_gemm_swiglu": ([vp, i64, i64, vp, vp, i32, i64, P, i64, vp, i64, vp],
@@ -325,6 +326,39 @@ def q4_gemm(A, W: Q4Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
         st = lib().q4_gemm(A.shape[0], _ptr(A), A.stride(0), None, ctypes.byref(wd), _ptr(C),
                            C.stride(0), _stream(stream))
     _check(st, "q4_gemm")
+    return C
+
+
+def q4_gemm_quantized(A, W: Q4Tensor, C: Q4Tensor, nv_global_in: Optional[torch.Tensor] = None,
+                      stream=None) -> Q4Tensor:
+    """The GEMM of q4_gemm with C written quantized by its epilogue (MXFP4,
+    or NVFP4 with the tensor scale nv_global_in): C holds what q4_quantize
+    writes for the bf16 product.  A is bf16 [M, K] (W tiled, any weight
+    format) or an MXFP4 tiled Q4Tensor (W MXFP4 tiled)."""
+    _q4(W, "W")
+    _q4(C, "C")
+    if isinstance(A, Q4Tensor):
+        _q4(A, "A")
+        if A.cols != W.cols:
+            raise ValueError(f"A has {A.cols} columns, W {W.cols}")
+        M = A.rows
+    else:
+        _matrix(A, "A", torch.bfloat16, 0, W.cols, exact_cols=True)
+        M = A.shape[0]
+    if C.rows != M or C.cols != W.rows:
+        raise ValueError(f"C must be {M} x {W.rows} (got {C.rows} x {C.cols})")
+    if nv_global_in is not None:
+        _vector(nv_global_in, "nv_global_in", torch.float32, 1)
+    _on_gpu(("W", W), ("A", A), ("C", C), ("nv_global_in", nv_global_in))
+    wd, cd = W.c(), C.c()
+    if isinstance(A, Q4Tensor):
+        ad = A.c()
+        st = lib().q4_gemm_quantized(M, None, 0, ctypes.byref(ad), ctypes.byref(wd), ctypes.byref(cd),
+                                     _ptr(nv_global_in), _stream(stream))
+    else:
+        st = lib().q4_gemm_quantized(M, _ptr(A), A.stride(0), None, ctypes.byref(wd), ctypes.byref(cd),
+                                     _ptr(nv_global_in), _stream(stream))
+    _check(st, "q4_gemm_quantized")
     return C
 
 

@@ -218,6 +218,51 @@ q4_status q4_gemm(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A
                                           as_stream(stream)));
 }
 
+q4_status q4_gemm_quantized(int64_t M, const void* A_bf16, int64_t lda, const q4_tensor* A_q,
+                            const q4_tensor* W, const q4_tensor* C_q, const float* nv_global_in,
+                            void* stream) {
+  q4_status st = check_tensor(W);
+  if (st != Q4_OK) return st;
+  st = check_tensor(C_q);
+  if (st != Q4_OK) return st;
+  if (W->fmt == Q4_FP8_ROW || W->layout != Q4_LAYOUT_TILED) return Q4_ERR_FORMAT;
+  if (C_q->fmt != Q4_MXFP4 && C_q->fmt != Q4_NVFP4) return Q4_ERR_FORMAT;
+  if (C_q->fmt == Q4_NVFP4) {
+    if (!nv_global_in) return Q4_ERR_NULL;
+    if (!aligned(nv_global_in, 4)) return Q4_ERR_ALIGN;
+  } else if (nv_global_in) {
+    return Q4_ERR_FORMAT;
+  }
+  if (M < 0 || M >= kMaxDim || M > (int64_t)65535 * 64) return Q4_ERR_SHAPE;
+  if ((A_bf16 == nullptr) == (A_q == nullptr)) return A_bf16 ? Q4_ERR_FORMAT : Q4_ERR_NULL;
+  const int64_t N = W->rows, K = W->cols;
+  if (C_q->rows != M || C_q->cols != N || N % 32) return Q4_ERR_SHAPE;
+  if (A_q) {
+    st = check_tensor(A_q);
+    if (st != Q4_OK) return st;
+    if (A_q->fmt != Q4_MXFP4 || W->fmt != Q4_MXFP4 || A_q->layout != Q4_LAYOUT_TILED) return Q4_ERR_FORMAT;
+    if (A_q->rows != M || A_q->cols != K) return Q4_ERR_SHAPE;
+  }
+  if (M == 0 || N == 0) return Q4_OK;
+  if (K == 0) return Q4_ERR_SHAPE;
+  if (!A_q) {
+    st = check_bf16(A_bf16, M, K, lda);
+    if (st != Q4_OK) return st;
+  }
+  const q4::QOut qo{static_cast<uint8_t*>(C_q->codes), static_cast<uint8_t*>(C_q->scales), nv_global_in,
+                    C_q->global_scale, C_q->layout == Q4_LAYOUT_TILED ? 1 : 0};
+  const int out = C_q->fmt == Q4_MXFP4 ? q4::kOutMxfp4 : q4::kOutNvfp4;
+  if (A_q)
+    return hip_status(q4::launch_gemm_w4a4_tiled_qout(
+        out, static_cast<const uint8_t*>(A_q->codes), static_cast<const uint8_t*>(A_q->scales), M,
+        static_cast<const uint8_t*>(W->codes), static_cast<const uint8_t*>(W->scales), N, K, qo,
+        as_stream(stream)));
+  return hip_status(q4::launch_gemm_w4a16_tiled_qout(W->fmt, out, static_cast<const uint8_t*>(W->codes),
+                                                     W->scales, W->global_scale, N, K,
+                                                     static_cast<const uint16_t*>(A_bf16), lda, M, qo,
+                                                     as_stream(stream)));
+}
+
 q4_status q4_grouped_gemm(const void* A_bf16, int64_t lda, int64_t T, const int32_t* gather,
                           const int32_t* expert_offsets, int32_t E, int64_t P,
                           const q4_tensor* W, int64_t N, void* C_bf16, int64_t ldc,

@@ -39,11 +39,13 @@
 //     visible and frees the buffer the next copies overwrite.  The loop is
 //     unrolled by 8 (one scale group) so every wait count is a constant.
 //   * weights are the matrix instruction's row operand, so a lane ends with
-//     4 consecutive columns of one row of C: 8-byte stores.
+//     4 consecutive columns of one row of C: 8-byte stores, or the
+//     quantized-output epilogue (q4_qout.h: C written as MXFP4 / NVFP4).
 #include "q4_launch.h"
 #include "q4_layout.h"
 #include "q4_lds.h"
 #include "q4_mma.h"
+#include "q4_qout.h"
 
 #include <type_traits>
 
@@ -66,12 +68,13 @@ constexpr int group_loads(int v) {
   return kAFrags / kWaves + (v % 2 == 0 ? kWTiles : 0) + (v % 8 == 0 ? kWTiles : 0);
 }
 
-template <int FMT>
+template <int FMT, int OUT>
 __global__ void __launch_bounds__(kWaves * 64)
 w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
                    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                    const float* __restrict__ gs_ptr, int N, int K, uint16_t* __restrict__ C,
-                   int64_t ldc) {
+                   int64_t ldc, QOut qo) {
+  qout_copy_gs<OUT>(qo);
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t (*abuf)[kAFrags][1024] = reinterpret_cast<uint8_t (*)[kAFrags][1024]>(smem);
   uint8_t (*wbuf)[kColTiles][1024] =
@@ -245,6 +248,10 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
   // tile (r, jj): lane l, register q holds C[m][n] with m = 16r + l%16 and
   // n = 16jj + 4(l/16) + q -- four consecutive columns of one row
   const int m0 = bm * 256 + (lane & 15);
+  if constexpr (OUT != kOutBf16) {
+    store_quantized<OUT>(acc, m0, bn * 256 + 16 * kWTiles * wave, M, N, qo, lane);
+    return;
+  }
   const int n0 = bn * 256 + 16 * kWTiles * wave + 4 * (lane >> 4);
 #pragma unroll
   for (int r = 0; r < kRowTiles; ++r) {
@@ -267,15 +274,25 @@ w4a16_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int M,
   }
 }
 
-template <int FMT>
+template <int FMT, int OUT = kOutBf16>
 hipError_t run(const uint16_t* A, int64_t lda, int64_t M, const uint8_t* codes, const void* scales,
-               const float* gs, int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
-  const hipError_t attr = set_max_lds<&w4a16_tiled_kernel<FMT>>(kSmemBytes);
+               const float* gs, int64_t N, int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream,
+               const QOut& qo = QOut{}) {
+  const hipError_t attr = set_max_lds<&w4a16_tiled_kernel<FMT, OUT>>(kSmemBytes);
   if (attr != hipSuccess) return attr;
   const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
-  w4a16_tiled_kernel<FMT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(
-      A, lda, (int)M, codes, static_cast<const uint8_t*>(scales), gs, (int)N, (int)K, C, ldc);
+  w4a16_tiled_kernel<FMT, OUT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(
+      A, lda, (int)M, codes, static_cast<const uint8_t*>(scales), gs, (int)N, (int)K, C, ldc, qo);
   return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t run_qout(int fmt, const uint16_t* A, int64_t lda, int64_t M, const uint8_t* codes, const void* scales,
+                    const float* gs, int64_t N, int64_t K, const QOut& qo, hipStream_t stream) {
+  if (fmt == 0) return run<0, OUT>(A, lda, M, codes, scales, gs, N, K, nullptr, 0, stream, qo);
+  if (fmt == 1) return run<1, OUT>(A, lda, M, codes, scales, gs, N, K, nullptr, 0, stream, qo);
+  if (fmt == 4) return run<4, OUT>(A, lda, M, codes, scales, gs, N, K, nullptr, 0, stream, qo);
+  return run<2, OUT>(A, lda, M, codes, scales, gs, N, K, nullptr, 0, stream, qo);
 }
 
 }  // namespace
@@ -288,6 +305,14 @@ hipError_t launch_gemm_w4a16_tiled(int fmt, const uint8_t* codes, const void* sc
   if (fmt == 1) return run<1>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
   if (fmt == 4) return run<4>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
   return run<2>(A, lda, M, codes, scales, gs, N, K, C, ldc, stream);
+}
+
+hipError_t launch_gemm_w4a16_tiled_qout(int w_fmt, int out_fmt, const uint8_t* codes, const void* scales,
+                                        const float* gs, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                        int64_t M, const QOut& qo, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (out_fmt == kOutMxfp4) return run_qout<kOutMxfp4>(w_fmt, A, lda, M, codes, scales, gs, N, K, qo, stream);
+  return run_qout<kOutNvfp4>(w_fmt, A, lda, M, codes, scales, gs, N, K, qo, stream);
 }
 
 }  // namespace q4

@@ -33,10 +33,15 @@
 //     unrolled by four so each wait count is a constant.
 //   * workgroups are ordered so that the 32 running on one XCD cover a
 //     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
+//   * the weight is the matrix instruction's row operand (C^T = W' A'^T per
+//     16x16 tile), so a lane ends with 4 consecutive columns of one row of
+//     C: one 8-byte store of bf16, or the quantized-output epilogue
+//     (q4_qout.h), which writes C as MXFP4 / NVFP4 codes and scales.
 #include "q4_launch.h"
 #include "q4_layout.h"
 #include "q4_lds.h"
 #include "q4_mma.h"
+#include "q4_qout.h"
 
 namespace q4 {
 namespace {
@@ -49,11 +54,13 @@ constexpr int kCopies = kTiles / kWaves;  // code tiles each wave copies per sta
 constexpr int kCodeBufs = 3;
 constexpr size_t kSmemBytes = kCodeBufs * kTiles * 1024 + 2 * kTiles * 256;  // 112 KB
 
+template <int OUT>
 __global__ void __launch_bounds__(kWaves * 64)
 w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
                   int M, const uint8_t* __restrict__ w_codes,
                   const uint8_t* __restrict__ w_scales, int N, int K,
-                  uint16_t* __restrict__ C, int64_t ldc) {
+                  uint16_t* __restrict__ C, int64_t ldc, QOut qo) {
+  qout_copy_gs<OUT>(qo);
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   uint8_t (*cbuf)[kTiles][1024] = reinterpret_cast<uint8_t (*)[kTiles][1024]>(smem);
   uint8_t (*sbuf)[kTiles][256] =
@@ -141,8 +148,8 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ea = (sa[i] >> (8 * j)) & 0xFF;
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], w, acc[i][jj], 4, 4, 0,
-                                                                      ea, 0, ew);
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a[i], acc[i][jj], 4, 4, 0,
+                                                                      ew, 0, ea);
       }
     }
   };
@@ -181,20 +188,50 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
   }
   wait_vmcnt<0>();
 
-  // lane l, register r of tile (i, jj) holds row 4(l/16) + r, column l%16
-  const int row0 = bm * 256 + wm * 128;
-  const int col0 = bn * 256 + wn * 64 + (lane & 15);
+  // lane l, register r of tile (i, jj) holds row 16i + l%16, column
+  // 16jj + 4(l/16) + r of the wave's 128 x 64 part
+  const int m0 = bm * 256 + wm * 128 + (lane & 15);
+  const int nw = bn * 256 + wn * 64;
+  if constexpr (OUT != kOutBf16) {
+    store_quantized<OUT>(acc, m0, nw, M, N, qo, lane);
+  } else {
+    const int n0 = nw + 4 * (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + 16 * i;
+      if (m < M) {
+        uint16_t* crow = C + (int64_t)m * ldc;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int n = col0 + jj * 16;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int n = n0 + 16 * jj;
+          const f32x4_t v = acc[i][jj];
+          if (n + 3 < N) {
+            store_bf16x4(crow + n, v[0], v[1], v[2], v[3]);
+          } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row0 + i * 16 + 4 * (lane >> 4) + r;
-        if (m < M && n < N) C[(int64_t)m * ldc + n] = (uint16_t)f32_to_bf16_rne(acc[i][jj][r]);
+            for (int r = 0; r < 4; ++r)
+              if (n + r < N) crow[n + r] = (uint16_t)f32_to_bf16_rne(v[r]);
+          }
+        }
       }
     }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+template <int OUT>
+hipError_t run(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, const uint8_t* w_codes,
+               const uint8_t* w_scales, int64_t N, int64_t K, uint16_t* C, int64_t ldc, const QOut& qo,
+               hipStream_t stream) {
+  const hipError_t attr = set_max_lds<&w4a4_tiled_kernel<OUT>>(kSmemBytes);
+  if (attr != hipSuccess) return attr;
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  w4a4_tiled_kernel<OUT><<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(a_codes, a_scales, (int)M, w_codes,
+                                                                   w_scales, (int)N, (int)K, C, ldc, qo);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -202,12 +239,15 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
 hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream) {
-  const hipError_t attr = set_max_lds<&w4a4_tiled_kernel>(kSmemBytes);
-  if (attr != hipSuccess) return attr;
-  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
-  w4a4_tiled_kernel<<<(unsigned)T, kWaves * 64, kSmemBytes, stream>>>(a_codes, a_scales, (int)M, w_codes,
-                                                              w_scales, (int)N, (int)K, C, ldc);
-  return hipGetLastError();
+  return run<kOutBf16>(a_codes, a_scales, M, w_codes, w_scales, N, K, C, ldc, QOut{}, stream);
+}
+
+hipError_t launch_gemm_w4a4_tiled_qout(int out_fmt, const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                                       const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
+                                       const QOut& qo, hipStream_t stream) {
+  if (out_fmt == kOutMxfp4)
+    return run<kOutMxfp4>(a_codes, a_scales, M, w_codes, w_scales, N, K, nullptr, 0, qo, stream);
+  return run<kOutNvfp4>(a_codes, a_scales, M, w_codes, w_scales, N, K, nullptr, 0, qo, stream);
 }
 
 }  // namespace q4

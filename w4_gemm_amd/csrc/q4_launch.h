@@ -27,6 +27,20 @@ hipError_t set_max_lds(size_t bytes) {
   return e;
 }
 
+// Output formats of the GEMMs that can write C quantized (q4_qout.h).
+constexpr int kOutBf16 = 0;
+constexpr int kOutMxfp4 = 1;
+constexpr int kOutNvfp4 = 2;
+
+// A quantized GEMM output (the C ABI's q4_tensor, as the kernels take it).
+struct QOut {
+  uint8_t* codes;
+  uint8_t* scales;
+  const float* gs_in;  // NVFP4: the tensor scale to quantize with (device)
+  float* gs_out;       // NVFP4: the output's own global-scale word (gets *gs_in)
+  int tiled;           // 1: tiled layout, 0: row-major
+};
+
 // Quantize bf16 src [rows][ld] into codes/scales (fmt 0 INT4 g128,
 // 1 MXFP4, 2 NVFP4; layout 0 row-major, 1 tiled).  NVFP4: gs receives the
 // global scale; gs_in, when not null, supplies it instead of the
@@ -66,6 +80,15 @@ hipError_t launch_gemm_w4a4(int a_layout, int w_layout, const uint8_t* a_codes, 
 hipError_t launch_gemm_w4a4_tiled(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
                                   const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                                   int64_t K, uint16_t* C, int64_t ldc, hipStream_t stream);
+
+// The same two GEMMs with C written quantized (MXFP4 or NVFP4 under the
+// tensor scale qo.gs_in, N % 32 == 0) by the epilogue of q4_qout.h.
+hipError_t launch_gemm_w4a16_tiled_qout(int w_fmt, int out_fmt, const uint8_t* codes, const void* scales,
+                                        const float* gs, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                        int64_t M, const QOut& qo, hipStream_t stream);
+hipError_t launch_gemm_w4a4_tiled_qout(int out_fmt, const uint8_t* a_codes, const uint8_t* a_scales, int64_t M,
+                                       const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
+                                       const QOut& qo, hipStream_t stream);
 
 // W4A4 NVFP4 GEMM C [M][ldc] = A' . W'^T, both NVFP4 (E4M3 per 16, each
 // operand's fp32 tensor scale a_gs / w_gs on the device), K % 128 == 0:

@@ -26,6 +26,7 @@
 // steps see the whole group.  In the tiled layout the padding rows of the
 // last tile are quantized as zeros.
 #include "q4_device.h"
+#include "q4_encode.h"
 #include "q4_launch.h"
 #include "q4_layout.h"
 
@@ -37,87 +38,6 @@ namespace q4 {
 namespace {
 
 constexpr int kThreads = 256;
-
-struct Chunk8 {
-  float v[8];
-};
-
-__device__ __forceinline__ Chunk8 load8(const uint16_t* p, bool valid) {
-  Chunk8 c;
-  uint4 raw = valid ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-  c.v[0] = bf16_lo(raw.x); c.v[1] = bf16_hi(raw.x);
-  c.v[2] = bf16_lo(raw.y); c.v[3] = bf16_hi(raw.y);
-  c.v[4] = bf16_lo(raw.z); c.v[5] = bf16_hi(raw.z);
-  c.v[6] = bf16_lo(raw.w); c.v[7] = bf16_hi(raw.w);
-  return c;
-}
-
-// Eight values -> eight packed E2M1 nibbles (element j in bits 4j..4j+3) of
-// value / scale, with scale a power of two.  v_cvt_scalef32_pk_fp4_f32
-// divides by 2^floor(log2 scale) (only the exponent of its scale operand is
-// used), rounds to the nearest E2M1 value with ties to the even code,
-// saturates to +-6 and keeps the sign bit -- the rounding rule of the
-// formats here, checked on gfx950 against every multiple of 1/128 in
-// [0, 10) including all the midpoints.
-__device__ __forceinline__ uint32_t e2m1_pack8(const Chunk8& c, float scale) {
-  uint32_t p = 0;
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[0], c.v[1], scale, 0);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[2], c.v[3], scale, 1);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[4], c.v[5], scale, 2);
-  p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, c.v[6], c.v[7], scale, 3);
-  return p;
-}
-
-// Division by a block scale.  Each code is a correctly rounded fp32
-// quotient w / s (NVFP4: also (amax / 6) / gs for the block scale) put
-// through a rounding to a short format (E2M1, E4M3, a clamped integer)
-// that is monotone in the value.  Here the quotient is formed as a product
-// with a reciprocal, twice, the product nudged down and up by a relative
-// 2^-20: the reciprocal (v_rcp_f32, within 1 ulp; an fp32 division, within
-// 1/2 ulp) and the products add under 2^-21 relative error in all, and the
-// fp32 quotient itself is within 2^-23 of the exact one (two roundings for
-// the block scale), so the two nudged products bracket it.  Where both
-// round to the same code, so does the quotient; where they differ (a
-// quotient within about 2^-20 of a rounding boundary, an exact tie) the
-// division is done.  This needs the operands in the normal range: the
-// callers take this path only for scales within [2^-100, 2^100]; a product
-// that overflows then stands for a quotient that takes the top code on
-// both sides, one that underflows for one that rounds to zero on both.
-constexpr float kNudgeDown = 1.0f - 0x1p-20f, kNudgeUp = 1.0f + 0x1p-20f;
-
-__device__ __forceinline__ bool in_bracket_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
-
-// E2M1 codes of x[j] / eff.
-__device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
-  if (in_bracket_range(eff)) {
-    const float r = __builtin_amdgcn_rcpf(eff);
-    const float rl = r * kNudgeDown, rh = r * kNudgeUp;
-    Chunk8 lo, hi;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo.v[j] = x.v[j] * rl;
-      hi.v[j] = x.v[j] * rh;
-    }
-    const uint32_t pl = e2m1_pack8(lo, 1.0f), ph = e2m1_pack8(hi, 1.0f);
-    if (__builtin_expect(pl == ph, 1)) return pl;
-  }
-  Chunk8 y;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) y.v[j] = x.v[j] / eff;  // fp32 division by the scale as used
-  return e2m1_pack8(y, 1.0f);
-}
-
-// E4M3 code of min((amax / 6) / gs, 448); rgs = 1 / gs (an fp32 division),
-// gs_ok = in_bracket_range(gs).
-__device__ __forceinline__ uint32_t nv_scale_code(float amax, float gs, float rgs, bool gs_ok) {
-  if (gs_ok) {
-    const float a = amax * rgs;
-    const uint32_t cl = e4m3_encode(fminf(a * (kNudgeDown / 6.0f), 448.0f));
-    const uint32_t ch = e4m3_encode(fminf(a * (kNudgeUp / 6.0f), 448.0f));
-    if (__builtin_expect(cl == ch, 1)) return cl;
-  }
-  return e4m3_encode(fminf((amax / 6.0f) / gs, 448.0f));
-}
 
 // INT4 codes, clamp(rne(w / s), -8, 7) or, with a zero point z in [-8, 7],
 // clamp(rne(w / s) + z, -8, 7), need no division.  A bf16 value (8
@@ -205,13 +125,6 @@ __device__ __forceinline__ ZpParams int4zp_params(float lo, float hi) {
 // Eight values -> eight INT4 nibbles with the zero point (codes 0 if s == 0).
 __device__ __forceinline__ uint32_t int4zp_pack8(const Chunk8& c, const ZpParams& zp) {
   return zp.s != 0.0f ? int4_pack8<true>(c, zp.s, (int)zp.z) : 0u;
-}
-
-__device__ __forceinline__ float absmax8(const Chunk8& c) {
-  float a = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(c.v[j]));
-  return a;
 }
 
 // FMT: 0 INT4 g128, 1 MXFP4, 2 NVFP4.  For NVFP4, gs_src holds the global
