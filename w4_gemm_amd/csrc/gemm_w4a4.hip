@@ -43,6 +43,8 @@
 #include "q4_mma.h"
 #include "q4_qout.h"
 
+#include <type_traits>
+
 namespace q4 {
 namespace {
 
@@ -120,71 +122,93 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint32_t sa[8], sw[4];
 
-  // math of stage s (j = s % 4 known at compile time)
-  auto compute = [&](int s, int j) {
-    const uint8_t(*cb)[1024] = cbuf[s % kCodeBufs];
-    if (j == 0) {
-      const uint8_t(*sb)[256] = sbuf[(s >> 2) & 1];
+  // Fragments in registers: the A fragments of the stage being multiplied
+  // (each reloaded with the next stage's as soon as its four products are
+  // issued), the W fragments of two stages (alternating), the scale words
+  // of the current and the next group of four stages (byte s % 4 of each is
+  // the stage's E8M0, picked by the matrix instruction's op_sel).
+  u32x4_t a[8], w[2][4];
+  uint32_t sa[8], sw[4], san[8], swn[4];
+  auto read_scales = [&](int t, uint32_t (&xa)[8], uint32_t (&xw)[4]) {
+    const uint8_t(*sb)[256] = sbuf[(t >> 2) & 1];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        sa[i] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + i][lane * 4]);
+    for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + i][lane * 4]);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        sw[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
-    }
-    i32x8_t a[8];
+    for (int jj = 0; jj < 4; ++jj) xw[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
+  };
+  auto read_w = [&](int t, u32x4_t (&dst)[4]) {
+    const uint8_t(*cb)[1024] = cbuf[t % kCodeBufs];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dst[jj] = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + jj][lane * 16]);
+  };
+  auto read_a = [&](int t, int i) {
+    return *reinterpret_cast<const u32x4_t*>(&cbuf[t % kCodeBufs][wm * 8 + i][lane * 16]);
+  };
+  auto as8 = [](u32x4_t v) { return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0}; };
+
+  // Iteration s (J = s % 4): wait until only copy group s+2 may be
+  // outstanding (group s+1 has landed) and this wave's reads of stage s+1's
+  // predecessor are done, barrier, issue group s+3 into the buffers of stage
+  // s (whose fragments every wave read in iteration s-1), then multiply
+  // stage s from registers while reading stage s+1's fragments: the W
+  // fragments first, then after the four products of each A fragment its
+  // successor.  Copies in group t: kCopies, plus the scale copy when
+  // t % 4 == 0.  (Past the last stage the reads fetch a buffer holding a
+  // clamped copy of the last stage: in bounds, never used.)
+  auto iteration = [&](int s, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int P = J & 1;
+    if constexpr (J == 2) wait_vmcnt_lgkm0<kCopies + 1>();
+    else wait_vmcnt_lgkm0<kCopies>();
+    stage_barrier();
+    issue_codes(s + 3);
+    if constexpr (J == 1) issue_scales(s + 3);
+    if constexpr (J == 3) read_scales(s + 1, san, swn);
+    read_w(s + 1, w[P ^ 1]);
+    // the copies, then the next stage's W fragment (and scale) reads, first
+    __builtin_amdgcn_sched_group_barrier(0x020, kCopies + (J == 1 ? 1 : 0), 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + (J == 3 ? 12 : 0), 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4_t va = *reinterpret_cast<const u32x4_t*>(&cb[wm * 8 + i][lane * 16]);
-      a[i] = i32x8_t{(int)va[0], (int)va[1], (int)va[2], (int)va[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as8(w[P][jj]), as8(a[i]), acc[i][jj], 4, 4,
+                                                                      J, sw[jj], J, sa[i]);
+      a[i] = read_a(s + 1, i);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // the four products of A fragment i
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the read of its successor
     }
+    if constexpr (J == 3) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + jj][lane * 16]);
-      const i32x8_t w = i32x8_t{(int)vw[0], (int)vw[1], (int)vw[2], (int)vw[3], 0, 0, 0, 0};
-      const int ew = (sw[jj] >> (8 * j)) & 0xFF;
+      for (int i = 0; i < 8; ++i) sa[i] = san[i];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ea = (sa[i] >> (8 * j)) & 0xFF;
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, a[i], acc[i][jj], 4, 4, 0,
-                                                                      ew, 0, ea);
-      }
+      for (int jj = 0; jj < 4; ++jj) sw[jj] = swn[jj];
     }
   };
 
-  // prologue: groups 0 (codes + scales) and 1 (codes)
+  // prologue: copy groups 0 (codes + scales), 1 and 2; stage 0 into registers
   issue_codes(0);
   issue_scales(0);
   issue_codes(1);
+  issue_codes(2);
+  wait_vmcnt_lgkm0<2 * kCopies>();
+  stage_barrier();
+  read_scales(0, sa, sw);
+  read_w(0, w[0]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = read_a(0, i);
 
-  // iteration s: wait for group s (group s+1 may stay in flight), barrier,
-  // issue group s+2 into the buffers of stage s-1, compute stage s.
-  // Copies in group s+1: kCopies, plus 1 when (s+1) % 4 == 0.
   // The tiled layout has K % 512 == 0, so S is a multiple of 4.
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
   for (int s0 = 0; s0 < S; s0 += 4) {
-    // j = 0
-    wait_vmcnt_lgkm0<kCopies>();
-    stage_barrier_loose();
-    issue_codes(s0 + 2);
-    compute(s0, 0);
-    // j = 1
-    wait_vmcnt_lgkm0<kCopies>();
-    stage_barrier_loose();
-    issue_codes(s0 + 3);
-    compute(s0 + 1, 1);
-    // j = 2: group s0+4 starts a new scale group
-    wait_vmcnt_lgkm0<kCopies>();
-    stage_barrier_loose();
-    issue_codes(s0 + 4);
-    issue_scales(s0 + 4);
-    compute(s0 + 2, 2);
-    // j = 3: group s0+4 (outstanding) also holds its scale copy
-    wait_vmcnt_lgkm0<kCopies + 1>();
-    stage_barrier_loose();
-    issue_codes(s0 + 5);
-    compute(s0 + 3, 3);
+    iteration(s0, J0());
+    iteration(s0 + 1, J1());
+    iteration(s0 + 2, J2());
+    iteration(s0 + 3, J3());
   }
   wait_vmcnt<0>();
 

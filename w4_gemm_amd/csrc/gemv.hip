@@ -24,11 +24,14 @@
 //     waves are spread over the matrix (tile = wave * workgroups +
 //     workgroup).
 //   * x is staged in LDS once per step by the whole workgroup (BT rows,
-//     double-buffered) and shared by its waves.  The next step's x loads are
-//     issued first, then its code loads (non-temporal: the weights are
-//     streamed once), then the current step's math runs, and only then are
-//     the x values written to LDS -- so the wait for x never waits for the
-//     weights, and one step of weights is always in flight.  The per-step
+//     double-buffered) and shared by its waves.  In each step the x loads of
+//     two steps ahead are issued first, then the code loads of the next step
+//     (non-temporal: the weights are streamed once), then the current step's
+//     math runs, and only then are the next step's x values -- loaded a step
+//     earlier -- written to LDS: loads complete in order, so by then they
+//     have landed, and one step of weights is always in flight.  (Loading x
+//     only one step ahead left its L2 latency exposed at B = 16: 21.4-22.7
+//     against 20.1-20.3 us on the 28672 x 8192 MXFP4 weight.)  The per-step
 //     barrier keeps a workgroup's waves in lockstep, which measured faster
 //     than letting them drift.
 //   * the loop bodies issue their loads unconditionally (the tail steps are
@@ -295,39 +298,45 @@ gemv_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
     for (int t = 0; t < TPW; ++t) ts[t].load(f[t], st);
   };
 
-  // two buffers; the next step's x loads are issued before its code loads
-  // and written to LDS after the current step's math
+  // two weight buffers; the x loads of step st+2 are issued before the code
+  // loads of step st+1
   StepFrag<FMT, LAYOUT> fa[TPW], fb[TPW];
   u32x4_t xr[XPER];
   // Issue order is pinned (scheduling barriers): the compiler would
-  // otherwise sink the next step's loads below the current step's math to
+  // otherwise sink the next steps' loads below the current step's math to
   // save registers -- and then wait for all of them before storing x.
-  auto prefetch = [&](StepFrag<FMT, LAYOUT> (&f)[TPW], int st) {
+  auto prefetch = [&](u32x4_t (&xd)[XPER], int xst, StepFrag<FMT, LAYOUT> (&f)[TPW], int wst) {
     __builtin_amdgcn_sched_barrier(0);
-    load_x(xr, st);
+    load_x(xd, xst);
     __builtin_amdgcn_sched_barrier(0);
-    load_w(f, st);
+    load_w(f, wst);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // x is loaded two steps ahead (two register sets, xr and xq): the values
+  // written to LDS after step st's math were loaded during step st-1, before
+  // the weights that step st's math already waited for (loads complete in
+  // order), so the write never waits; weights are loaded one step ahead.
+  u32x4_t xq[XPER];
   load_x(xr, 0);
+  load_x(xq, 1);
   load_w(fa, 0);
   store_x(xr, 0, 0);
   __syncthreads();
   int st = 0;
   for (; st + 2 < nst; st += 2) {
-    prefetch(fb, st + 1);
+    prefetch(xr, st + 2, fb, st + 1);
     step_math<FMT, LAYOUT, TPW>(fa, xrow(st & 1), gs, acc);
-    store_x(xr, (st + 1) & 1, st + 1);
+    store_x(xq, (st + 1) & 1, st + 1);
     __syncthreads();
-    prefetch(fa, st + 2);
+    prefetch(xq, st + 3, fa, st + 2);
     step_math<FMT, LAYOUT, TPW>(fb, xrow((st + 1) & 1), gs, acc);
     store_x(xr, st & 1, st + 2);
     __syncthreads();
   }
-  if (st + 1 < nst) {  // two steps left
-    prefetch(fb, st + 1);
+  if (st + 1 < nst) {  // two steps left (xq holds step st+1)
+    load_w(fb, st + 1);
     step_math<FMT, LAYOUT, TPW>(fa, xrow(st & 1), gs, acc);
-    store_x(xr, (st + 1) & 1, st + 1);
+    store_x(xq, (st + 1) & 1, st + 1);
     __syncthreads();
     step_math<FMT, LAYOUT, TPW>(fb, xrow((st + 1) & 1), gs, acc);
   } else {             // one step left
