@@ -204,11 +204,12 @@ template <int FMT, int LAYOUT>
 __global__ void __launch_bounds__(kThreads)
 quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
                       uint8_t* __restrict__ codes, void* __restrict__ scales,
-                      const float* gs_src, float* gs_out) {
+                      const float* gs_src, float* gs_out, int reverse) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[16][512 + 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t KB = (cols + 511) >> 9;
-  const int64_t band = blockIdx.x / KB, kb = blockIdx.x - band * KB;
+  const int64_t b0 = blockIdx.x / KB, kb = blockIdx.x - b0 * KB;
+  const int64_t band = reverse ? (int64_t)gridDim.x / KB - 1 - b0 : b0;
   const int64_t r0 = band * 16, k0 = kb * 512;
 
   float gs = 0.0f;
@@ -485,13 +486,14 @@ unsigned grid_for(int64_t chunks) {
 
 // Quantize kernel launch: the block-mapped kernel when cols % 128 == 0,
 // else the lane-per-8-values kernel.
+// reverse = 1 walks the row bands last to first (see the NVFP4 path).
 template <int FMT, int LAYOUT>
 void launch_q(const uint16_t* src, int64_t ld, int64_t rows, int64_t cols, uint8_t* codes,
-              void* scales, const float* gs_src, float* gs_out, hipStream_t stream) {
+              void* scales, const float* gs_src, float* gs_out, hipStream_t stream, int reverse = 0) {
   if (cols % 128 == 0) {
     const int64_t blocks = ((stored_rows<LAYOUT>(rows) + 15) / 16) * ((cols + 511) / 512);
     quantize_block_kernel<FMT, LAYOUT><<<(unsigned)blocks, kThreads, 0, stream>>>(
-        src, ld, rows, cols, codes, scales, gs_src, gs_out);
+        src, ld, rows, cols, codes, scales, gs_src, gs_out, reverse);
   } else {
     const unsigned grid = grid_for(stored_rows<LAYOUT>(rows) * (cols >> 3));
     quantize_kernel<FMT, LAYOUT><<<grid, kThreads, 0, stream>>>(src, ld, rows, cols, codes, scales,
@@ -534,7 +536,9 @@ hipError_t quantize_layout(int fmt, const uint16_t* src, int64_t ld, int64_t row
           const unsigned agrid = (unsigned)(rows < 256 ? rows : 256);
           absmax_kernel<<<agrid, kThreads, 0, stream>>>(src, ld, rows, cols, gs_bits);
         }
-        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, nullptr, stream);
+        // the absmax pass reads the rows first to last, so the last ones
+        // are still in the last-level cache: the block pass starts there
+        launch_q<2, LAYOUT>(src, ld, rows, cols, codes, scales, gs, nullptr, stream, 1);
       }
     }
   }
