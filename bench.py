@@ -219,6 +219,15 @@ def main():
                 traffic = rec["bytes_per_launch"][str(dom)]
         except Exception:
             traffic = None
+    # the read ceiling: a plain streaming read (q4_read_probe) of a buffer of
+    # the weight's size, rotating six copies past the last-level cache as the
+    # GEMV does -- the rate the GEMV can approach on this part
+    rbufs = [torch.full((wbytes,), i + 1, dtype=torch.uint8, device=dev) for i in range(ncopy)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    rgt = GraphTimer(torch, lambda i: q4.q4_read_probe(rbufs[i % ncopy], sink), per_graph=ncopy * 4)
+    read_ms = rgt.per_launch_ms(max(3, args.steps // (ncopy * 4)))
+    read_gbs = wbytes / (read_ms * 1e-3) / 1e9
+    del rbufs, rgt
     # a measured device-to-device copy of 1 GB (1 GB read + 1 GB written),
     # reported beside the published peak as context
     csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -230,6 +239,9 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"gemv_kernel<MXFP4> B={dom}", "alg_bytes_per_launch": per_b[dom]["alg_bytes"],
                 "avg_launch_us": round(per_b[dom]["us"], 3),
+                "read_ceiling_GBps": round(read_gbs, 1), "read_ceiling_us": round(read_ms * 1e3, 3),
+                "read_ceiling_bytes": wbytes,
+                "frac_of_read_ceiling": round(achieved / read_gbs, 4),
                 "device_copy_GBps": round(copy_gbs, 1),
                 "frac_of_device_copy": round(achieved / copy_gbs, 4)}
 

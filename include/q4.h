@@ -330,6 +330,20 @@ q4_status q4_swiglu(const void* gu_bf16, int64_t ld_gu, int64_t P, int64_t I, vo
 q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, const float* weights,
                          int64_t T, int32_t k, int64_t N, void* out_bf16, int64_t ldo, void* stream);
 
+/*
+ * Measurement helper, not a step of the method: reads `bytes` of device
+ * memory at src with a plain streaming kernel (16-byte non-temporal loads,
+ * each wave 8 KB in flight) and discards the data.  Decode GEMVs are bound
+ * by their weight reads ("Low-bit inference for very large MoE", table
+ * "Kernels on different hardware", row W4A16), so timing this read on a
+ * buffer of the weight's size gives the rate the GEMV can approach on this
+ * part.  src 16-byte aligned, bytes a multiple of 1024 (else Q4_ERR_ALIGN /
+ * Q4_ERR_SHAPE); sink: device uint32[1], written only if the folded data
+ * equals one fixed 32-bit constant (which keeps the loads alive).
+ * bytes == 0 is a no-op.
+ */
+q4_status q4_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -246,3 +246,14 @@ def test_gemm_quantized_validation():
     assert R(64, A_ODD, 512, None, by(w), by(c), None) == ALIGN
     assert R(32, None, 0, by(a), by(wmx), by(c), None) == SHAPE              # A rows != M
     assert R(0, A16, 512, None, by(w), by(desc(rows=0, cols=512)), None) == OK
+
+
+def test_read_probe_validation():
+    L = q4.lib()
+    assert L.q4_read_probe(A16, 1000, A16, None) == SHAPE
+    assert L.q4_read_probe(A16, -1024, A16, None) == SHAPE
+    assert L.q4_read_probe(None, 1024, A16, None) == NULL
+    assert L.q4_read_probe(A16, 1024, None, None) == NULL
+    assert L.q4_read_probe(A16 + 4, 1024, A16, None) == ALIGN
+    assert L.q4_read_probe(A16, 1024, A16 + 2, None) == ALIGN
+    assert L.q4_read_probe(None, 0, None, None) == OK

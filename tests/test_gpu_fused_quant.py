@@ -136,3 +136,4 @@ def test_w4a4_chain_full_size():
     q4.q4_gemm(qg, W, C3)
     torch.cuda.synchronize()
     assert torch.equal(C2, C3)
+

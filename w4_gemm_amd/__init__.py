@@ -22,7 +22,7 @@ __all__ = [
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
-    "moe_layer", "interleave_gate_up",
+    "moe_layer", "interleave_gate_up", "q4_read_probe",
     "empty_q4", "quantize", "LIB_PATH",
 ]
 
@@ -88,6 +88,7 @@ def _lib_handle():
             "q4_moe_route": ([vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "q4_swiglu": ([vp, i64, i64, i64, vp, i64, vp], ctypes.c_int),
             "q4_moe_combine": ([vp, i64, vp, vp, i64, i32, i64, vp, i64, vp], ctypes.c_int),
+            "q4_read_probe": ([vp, i64, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -464,6 +465,19 @@ def q4_grouped_gemm_swiglu(A: torch.Tensor, gather: Optional[torch.Tensor], offs
                                         ctypes.byref(wd), inter, _ptr(H), H.stride(0), _stream(stream)),
            "q4_grouped_gemm_swiglu")
     return H
+
+
+def q4_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: stream-read all of src (a contiguous GPU tensor of
+    a multiple of 1024 bytes) and discard it (sink: int32 GPU tensor [1])."""
+    if not isinstance(src, torch.Tensor) or not src.is_contiguous():
+        raise ValueError("src must be a contiguous tensor")
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 1024:
+        raise ValueError("src must hold a multiple of 1024 bytes")
+    _vector(sink, "sink", torch.int32, 1)
+    _on_gpu(("src", src), ("sink", sink))
+    _check(lib().q4_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "q4_read_probe")
 
 
 def interleave_gate_up(w_gu: torch.Tensor, experts: int, inter: int) -> torch.Tensor:

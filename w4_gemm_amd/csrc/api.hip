@@ -362,4 +362,12 @@ q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, co
                                            static_cast<uint16_t*>(out_bf16), ldo, as_stream(stream)));
 }
 
+q4_status q4_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 1024) return Q4_ERR_SHAPE;
+  if (bytes == 0) return Q4_OK;
+  if (!src || !sink) return Q4_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return Q4_ERR_ALIGN;
+  return hip_status(q4::launch_read_probe(static_cast<const uint8_t*>(src), bytes, sink, as_stream(stream)));
+}
+
 }  // extern "C"

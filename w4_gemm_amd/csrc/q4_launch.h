@@ -41,6 +41,10 @@ struct QOut {
   int tiled;           // 1: tiled layout, 0: row-major
 };
 
+// Plain streaming read of `bytes` (a multiple of 1024) at src (16-byte
+// aligned); `sink` (device uint32) is never written by real data.
+hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Quantize bf16 src [rows][ld] into codes/scales (fmt 0 INT4 g128,
 // 1 MXFP4, 2 NVFP4; layout 0 row-major, 1 tiled).  NVFP4: gs receives the
 // global scale; gs_in, when not null, supplies it instead of the
