@@ -19,18 +19,20 @@
 //   * K advances in stages of one super-chunk (128 k).  A stage needs 16
 //     A tiles and 16 W tiles (32 KB); they are copied verbatim into LDS by
 //     direct global->LDS loads (global_load_lds_dwordx4: one 1 KB tile per
-//     wave instruction, no registers; 4 per wave), two stages ahead, into
-//     three buffers.  Scales are copied per group of four stages (16 x 256 B for
-//     each operand) into two buffers.  Every fragment read from LDS is one
+//     wave instruction, no registers; 4 per wave), three stages ahead, into
+//     four buffers (144 KB of LDS with the scales: one workgroup per CU).
+//     Scales are copied per group of four stages (16 x 256 B for each
+//     operand) into two buffers.  Every fragment read from LDS is one
 //     contiguous kilobyte (conflict-free).
 //   * one barrier per stage: each wave first waits for its own copies of
-//     the current stage (explicit vmcnt) and for every LDS read it has
-//     issued (lgkmcnt 0), so the fragments of the previous stage are in
-//     registers; the barrier then makes every wave's copies visible, and
-//     the buffer the next copies overwrite -- the previous stage's -- is no
-//     longer read by any wave, whatever the compiler does with the matrix
-//     instructions that consume those registers.  The stage loop is
-//     unrolled by four so each wait count is a constant.
+//     the next stage (explicit vmcnt); the barrier then makes every wave's
+//     copies visible.  The copies issued after it overwrite the buffer of
+//     the stage before the current one, whose fragments every wave read
+//     during the stage before that and consumed in the matrix instructions
+//     of the previous stage -- before this barrier in program order -- so
+//     no wave still reads it, and no wave has to drain its LDS reads before
+//     the barrier.  The stage loop is unrolled by four so each wait count
+//     is a constant.
 //   * workgroups are ordered so that the 32 running on one XCD cover a
 //     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
 //   * the weight is the matrix instruction's row operand (C^T = W' A'^T per
@@ -53,8 +55,8 @@ constexpr int kBN = 16;          // W tiles per workgroup
 constexpr int kTiles = kBM + kBN;
 constexpr int kWaves = 8;
 constexpr int kCopies = kTiles / kWaves;  // code tiles each wave copies per stage
-constexpr int kCodeBufs = 3;
-constexpr size_t kSmemBytes = kCodeBufs * kTiles * 1024 + 2 * kTiles * 256;  // 112 KB
+constexpr int kCodeBufs = 4;
+constexpr size_t kSmemBytes = kCodeBufs * kTiles * 1024 + 2 * kTiles * 256;  // 144 KB
 
 template <int OUT>
 __global__ void __launch_bounds__(kWaves * 64)
@@ -148,36 +150,55 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
   auto as8 = [](u32x4_t v) { return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0}; };
 
   // Iteration s (J = s % 4): wait until only copy group s+2 may be
-  // outstanding (group s+1 has landed) and this wave's reads of stage s+1's
-  // predecessor are done, barrier, issue group s+3 into the buffers of stage
-  // s (whose fragments every wave read in iteration s-1), then multiply
-  // stage s from registers while reading stage s+1's fragments: the W
-  // fragments first, then after the four products of each A fragment its
-  // successor.  Copies in group t: kCopies, plus the scale copy when
-  // t % 4 == 0.  (Past the last stage the reads fetch a buffer holding a
-  // clamped copy of the last stage: in bounds, never used.)
+  // outstanding (group s+1 has landed), barrier, then multiply stage s from
+  // registers while reading stage s+1's fragments: after the four products
+  // of A fragment i, its successor, and for i < 4 also W fragment i of the
+  // next stage (the other register set); after the products of A fragment 0
+  // the copies of group s+3 (into the buffer of stage s-1); when J == 3,
+  // after A fragments 4..6, the next group's scale words.  Reading the next
+  // stage's W fragments after the first products rather than before them
+  // keeps every fragment a product needs at most 11 LDS reads back, so its
+  // wait is a count, not a drain of the reads just issued.  Copies in group
+  // t: kCopies, plus the scale copy when t % 4 == 0.  (Past the last stage
+  // the reads fetch a buffer holding a clamped copy of the last stage: in
+  // bounds, never used.)
   auto iteration = [&](int s, auto jc) {
     constexpr int J = decltype(jc)::value;
     constexpr int P = J & 1;
-    if constexpr (J == 2) wait_vmcnt_lgkm0<kCopies + 1>();
-    else wait_vmcnt_lgkm0<kCopies>();
+    if constexpr (J == 2) wait_vmcnt<kCopies + 1>();
+    else wait_vmcnt<kCopies>();
     stage_barrier();
-    issue_codes(s + 3);
-    if constexpr (J == 1) issue_scales(s + 3);
-    if constexpr (J == 3) read_scales(s + 1, san, swn);
-    read_w(s + 1, w[P ^ 1]);
-    // the copies, then the next stage's W fragment (and scale) reads, first
-    __builtin_amdgcn_sched_group_barrier(0x020, kCopies + (J == 1 ? 1 : 0), 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + (J == 3 ? 12 : 0), 0);
+    const uint8_t(*cb)[1024] = cbuf[(s + 1) % kCodeBufs];
+    const uint8_t(*sb)[256] = sbuf[((s + 1) >> 2) & 1];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as8(w[P][jj]), as8(a[i]), acc[i][jj], 4, 4,
                                                                       J, sw[jj], J, sa[i]);
-      a[i] = read_a(s + 1, i);
+      a[i] = *reinterpret_cast<const u32x4_t*>(&cb[wm * 8 + i][lane * 16]);
+      if (i < 4) w[P ^ 1][i] = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + i][lane * 16]);
+      if constexpr (J == 3) {
+        if (i == 4 || i == 5) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            san[4 * (i - 4) + r] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + 4 * (i - 4) + r][lane * 4]);
+        }
+        if (i == 6) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) swn[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
+        }
+      }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // the four products of A fragment i
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the read of its successor
+      if (i == 0) {
+        issue_codes(s + 3);
+        if constexpr (J == 1) issue_scales(s + 3);
+        __builtin_amdgcn_sched_group_barrier(0x020, kCopies + (J == 1 ? 1 : 0), 0);
+      }
+      // then the LDS reads issued above
+      if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (J == 3 && i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     if constexpr (J == 3) {
 #pragma unroll
