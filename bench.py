@@ -114,6 +114,41 @@ def timed(torch, fn, iters, warmup=1, replays=3):
     return g.per_launch_ms(replays, warmup=warmup)
 
 
+_MFMA_CEILING = {}
+
+
+def mfma_ceiling(torch, q4, dev, kind):
+    """TFLOP/s this part sustains for one kind of matrix instruction on
+    random register operands (q4_mfma_probe, two waves per SIMD on every
+    CU): the ceiling of a GEMM built on that instruction.  Random operands
+    make the part lower its clock to stay within its power limit, so this is
+    below the published dense peak.  Measured once per kind, after a short
+    idle gap, over about 0.2 s of back-to-back launches."""
+    if kind not in _MFMA_CEILING:
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        iters = 4096 if kind in ("fp4", "fp8") else 8192
+        flops = [0.0]
+
+        def fn():
+            flops[0] = q4.q4_mfma_probe(kind, iters, sink)
+
+        torch.cuda.synchronize()
+        time.sleep(IDLE_GAP_S)
+        ms = timed(torch, fn, 20, warmup=10, replays=5)
+        _MFMA_CEILING[kind] = flops[0] / (ms * 1e-3) / 1e12
+    return _MFMA_CEILING[kind]
+
+
+def with_ceiling(res, torch, q4, dev, kind, keys=("TFLOPs",)):
+    """Adds the measured ceiling of `kind` and each rate's fraction of it."""
+    c = mfma_ceiling(torch, q4, dev, kind)
+    res["mfma_ceiling_TFLOPs"] = round(c, 1)
+    res["mfma_ceiling_kind"] = kind
+    for k in keys:
+        res["frac_mfma_ceiling" if k == "TFLOPs" else f"frac_mfma_ceiling_{k}"] = round(res[k] / c, 4)
+    return res
+
+
 def cpu_cores():
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     omp = os.environ.get("OMP_NUM_THREADS")
@@ -332,6 +367,13 @@ def main():
             time.sleep(IDLE_GAP_S)
             extra[key] = fn()
 
+    if _MFMA_CEILING:
+        extra["mfma_ceilings_TFLOPs"] = {
+            k: {"measured": round(v, 1), "published_peak": {"fp4": FP4_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS,
+                                                          "fp16": FP16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS}[k],
+                "note": "random register operands, q4_mfma_probe"}
+            for k, v in _MFMA_CEILING.items()}
+
     cpu = None
     if not args.no_cpu_baseline:
         del copies
@@ -386,10 +428,11 @@ def bench_nvfp4(torch, q4, workloads, dev, seed):
     ms = timed(torch, lambda: q4.q4_gemm(A, q, C), 10, 2)
     qms = timed(torch, lambda: q4.q4_quantize(W, q), 10, 2)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
-            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-            "quantize_us": round(qms * 1e3, 1),
-            "quantize_GBps": round((N * K * 2 * 2 + q.nbytes) / (qms * 1e-3) / 1e9, 1)}
+    res = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+           "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+           "quantize_us": round(qms * 1e3, 1),
+           "quantize_GBps": round((N * K * 2 * 2 + q.nbytes) / (qms * 1e-3) / 1e9, 1)}
+    return with_ceiling(res, torch, q4, dev, "bf16")
 
 
 def bench_moe(torch, q4, workloads, dev, seed):
@@ -512,7 +555,8 @@ def bench_w4a4(torch, q4, workloads, dev, seed, fmt="mxfp4"):
         res["layer_with_fused_act_quantize_us"] = round(fms * 1e3, 1)
         res["fused_epilogue_saves_us"] = round((ums - fms) * 1e3, 1)
         res["fused_TFLOPs"] = round(2.0 * M * N * K / (fms * 1e-3) / 1e12, 1)
-    return res
+        return with_ceiling(res, torch, q4, dev, "fp4", ("TFLOPs", "fused_TFLOPs"))
+    return with_ceiling(res, torch, q4, dev, "fp16")
 
 
 def bench_w4a8(torch, q4, workloads, dev, seed):
@@ -528,10 +572,11 @@ def bench_w4a8(torch, q4, workloads, dev, seed):
     ms = timed(torch, lambda: q4.q4_gemm(qa, qw, C), 10, 2)
     ams = timed(torch, lambda: q4.q4_quantize(A, qa), 10, 2)
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-    return {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
-            "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
-            "act_quantize_us": round(ams * 1e3, 1),
-            "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+    res = {"gemm_us": round(ms * 1e3, 1), "TFLOPs": round(tflops, 1),
+           "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+           "act_quantize_us": round(ams * 1e3, 1),
+           "act_quantize_GBps": round((M * K * 2 + qa.nbytes) / (ams * 1e-3) / 1e9, 1)}
+    return with_ceiling(res, torch, q4, dev, "fp8")
 
 
 def cpu_model():

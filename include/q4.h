@@ -344,6 +344,37 @@ q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, co
  */
 q4_status q4_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Measurement helper, not a step of the method: the rate at which this part
+ * sustains one kind of matrix instruction, back to back, with operands in
+ * registers -- the ceiling a GEMM built on that instruction can approach.
+ * The operands are pseudo-random bits drawn from `seed` (as quantized data
+ * is): with random operands the part lowers its clock to stay within its
+ * power limit, so this rate lies below the published dense peak.
+ *   kind   Q4_PROBE_FP4  scaled 16x16x128 with E2M1 operands (the W4A4
+ *                        MXFP4 GEMM's instruction)
+ *          Q4_PROBE_BF16 16x16x32 bf16 (GEMV, W4A16 GEMM, grouped GEMM)
+ *          Q4_PROBE_F16  16x16x32 fp16 (the NVFP4 W4A4 GEMM)
+ *          Q4_PROBE_FP8  scaled 16x16x128 with E4M3 operands (W4A8)
+ *          other values: Q4_ERR_FORMAT
+ *   iters  iterations of 8 instructions per wave, 0 .. 2^24 (else
+ *          Q4_ERR_SHAPE); the launch runs two waves per SIMD on every
+ *          compute unit; iters == 0 is a no-op (*flops = 0)
+ *   sink   device uint32[1], written only if the folded sums equal one
+ *          fixed constant (which keeps the products alive)
+ *   flops  host double: receives the floating-point operations the launch
+ *          performs (2*16*16*K per instruction); NULL: Q4_ERR_NULL
+ */
+typedef enum q4_probe_kind {
+    Q4_PROBE_FP4 = 0,
+    Q4_PROBE_BF16 = 1,
+    Q4_PROBE_F16 = 2,
+    Q4_PROBE_FP8 = 3
+} q4_probe_kind;
+
+q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* sink, double* flops,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -248,6 +248,25 @@ def test_gemm_quantized_validation():
     assert R(0, A16, 512, None, by(w), by(desc(rows=0, cols=512)), None) == OK
 
 
+def test_mfma_probe_validation():
+    """Argument checks of the matrix-instruction probe; iters == 0 returns
+    before any device query, so this runs without a GPU."""
+    import ctypes
+    L = q4.lib()
+    f = ctypes.c_double(-1.0)
+    assert L.q4_mfma_probe(4, 1, 0, A16, ctypes.byref(f), None) == FMT
+    assert L.q4_mfma_probe(-1, 1, 0, A16, ctypes.byref(f), None) == FMT
+    assert L.q4_mfma_probe(0, -1, 0, A16, ctypes.byref(f), None) == SHAPE
+    assert L.q4_mfma_probe(0, (1 << 24) + 1, 0, A16, ctypes.byref(f), None) == SHAPE
+    assert L.q4_mfma_probe(0, 1, 0, A16, None, None) == NULL
+    assert L.q4_mfma_probe(1, 1, 0, None, ctypes.byref(f), None) == NULL
+    assert L.q4_mfma_probe(1, 1, 0, A16 + 2, ctypes.byref(f), None) == ALIGN
+    for kind in range(4):
+        f.value = -1.0
+        assert L.q4_mfma_probe(kind, 0, 0, None, ctypes.byref(f), None) == OK
+        assert f.value == 0.0
+
+
 def test_read_probe_validation():
     L = q4.lib()
     assert L.q4_read_probe(A16, 1000, A16, None) == SHAPE

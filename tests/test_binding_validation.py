@@ -142,3 +142,12 @@ def test_moe_helpers_reject():
     bad = q4.Routing(r.ids, r.weights.double(), r.offsets, r.gather, r.inv)
     _raises("r.weights must be a torch.float32", q4.q4_moe_combine, y, bad)
     _raises("must be a GPU tensor", q4.q4_moe_combine, y, r, torch.zeros(T, N, dtype=BF16))
+
+
+def test_mfma_probe_rejects():
+    sink = torch.zeros(1, dtype=I32)
+    _raises("kind must be one of", q4.q4_mfma_probe, "int8", 16, sink)
+    _raises("iters must be an int", q4.q4_mfma_probe, "fp4", -1, sink)
+    _raises("iters must be an int", q4.q4_mfma_probe, "fp4", 1.5, sink)
+    _raises("sink must be a torch.int32", q4.q4_mfma_probe, "fp4", 16, sink.float())
+    _raises("must be a GPU tensor", q4.q4_mfma_probe, "bf16", 16, sink)

@@ -1,5 +1,7 @@
-"""GPU check of the measurement helper q4_read_probe (the plain streaming
-read the benchmark times as the decode GEMV's read ceiling)."""
+"""GPU checks of the measurement helpers: q4_read_probe (the plain
+streaming read the benchmark times as the decode GEMV's read ceiling) and
+q4_mfma_probe (back-to-back matrix instructions on random operands: the
+GEMMs' measured ceiling)."""
 import pytest
 import torch
 
@@ -19,3 +21,28 @@ def test_read_probe_reads_and_leaves_sink():
         q4.q4_read_probe(buf, sink)
         torch.cuda.synchronize()
         assert int(sink.item()) == 7
+
+
+@pytest.mark.parametrize("kind,peak", [("fp4", 10100.0), ("bf16", 2500.0), ("fp16", 2500.0), ("fp8", 5000.0)])
+def test_mfma_probe_rate(kind, peak):
+    """The probe reports its operation count, leaves the sink alone, and
+    runs at a positive rate no higher than the published dense peak (plus
+    timing slack)."""
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    iters = 512
+    flops = q4.q4_mfma_probe(kind, iters, sink)
+    per = 2 * 16 * 16 * (128 if kind in ("fp4", "fp8") else 32)
+    waves = flops / (iters * 8 * per)
+    assert waves == int(waves) and int(waves) % 8 == 0 and waves > 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        q4.q4_mfma_probe(kind, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 5 * flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    print(f"{kind}: {tflops:.0f} TFLOP/s", flush=True)
+    assert 0 < tflops < 1.05 * peak
+    assert int(sink.item()) == 7
+    assert q4.q4_mfma_probe(kind, 0, sink) == 0.0

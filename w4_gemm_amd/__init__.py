@@ -22,7 +22,7 @@ __all__ = [
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
-    "moe_layer", "interleave_gate_up", "q4_read_probe",
+    "moe_layer", "interleave_gate_up", "q4_read_probe", "q4_mfma_probe", "PROBE_KINDS",
     "empty_q4", "quantize", "LIB_PATH",
 ]
 
@@ -89,6 +89,8 @@ def _lib_handle():
             "q4_swiglu": ([vp, i64, i64, i64, vp, i64, vp], ctypes.c_int),
             "q4_moe_combine": ([vp, i64, vp, vp, i64, i32, i64, vp, i64, vp], ctypes.c_int),
             "q4_read_probe": ([vp, i64, vp, vp], ctypes.c_int),
+            "q4_mfma_probe": ([ctypes.c_int32, i64, ctypes.c_uint32, vp, ctypes.POINTER(ctypes.c_double), vp],
+                              ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -478,6 +480,25 @@ def q4_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _vector(sink, "sink", torch.int32, 1)
     _on_gpu(("src", src), ("sink", sink))
     _check(lib().q4_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "q4_read_probe")
+
+
+PROBE_KINDS = {"fp4": 0, "bf16": 1, "fp16": 2, "fp8": 3}
+
+
+def q4_mfma_probe(kind: str, iters: int, sink: torch.Tensor, seed: int = 1, stream=None) -> float:
+    """Measurement helper: back-to-back matrix instructions of one kind
+    ("fp4", "bf16", "fp16", "fp8") on random register operands; returns the
+    launch's floating-point operations (sink: int32 GPU tensor [1])."""
+    if kind not in PROBE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(PROBE_KINDS)}")
+    if not isinstance(iters, int) or iters < 0 or iters > (1 << 24):
+        raise ValueError("iters must be an int in [0, 2^24]")
+    _vector(sink, "sink", torch.int32, 1)
+    _on_gpu(("sink", sink))
+    flops = ctypes.c_double(0.0)
+    _check(lib().q4_mfma_probe(PROBE_KINDS[kind], iters, seed & 0xFFFFFFFF, _ptr(sink), ctypes.byref(flops),
+                               _stream(stream)), "q4_mfma_probe")
+    return flops.value
 
 
 def interleave_gate_up(w_gu: torch.Tensor, experts: int, inter: int) -> torch.Tensor:

@@ -13,6 +13,17 @@
 // the loads from being removed.  The shape is the best of a sweep on gfx950
 // (pieces in flight 4/8/16, plain / non-temporal / global->LDS loads,
 // 512..2048 workgroups).
+//
+// The second probe is the matrix-core counterpart: the rate at which this
+// part sustains one kind of matrix instruction, back to back, on operands
+// already in registers.  The operands are pseudo-random bits (as quantized
+// weights and activations are): with constant operands the part holds its
+// top clock, with random ones it lowers the clock to stay within its power
+// limit, so the published peak is not the rate a GEMM on real data can
+// approach.  Each wave issues 8 independent instructions per iteration
+// (each accumulator is reused 8 instructions later), two waves per SIMD.
+// The instructions are written out so that every accumulator stays in
+// place: nothing else runs in the loop.
 #include "q4_launch.h"
 #include "q4_mma.h"
 
@@ -44,7 +55,103 @@ read_probe_kernel(const uint8_t* __restrict__ p, int64_t nchunks, uint32_t* __re
   if (w == kProbeMagic) sink[0] = w;
 }
 
+constexpr int kMfmaProbeWaves = 4;
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// KIND: 0 FP4 16x16x128 (scaled), 1 bf16 16x16x32, 2 fp16 16x16x32, 3 FP8 16x16x128 (scaled)
+template <int KIND>
+__global__ void __launch_bounds__(kMfmaProbeWaves * 64)
+mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
+  const uint32_t base = (seed * 0x9E3779B1u) ^ ((blockIdx.x * blockDim.x + threadIdx.x) * 64u);
+  u32x4_t x[8], y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t a = probe_hash(base + 8u * i + e), b = probe_hash(base + 8u * i + 4u + e + 0x51ED27u);
+      if constexpr (KIND == 1) {  // bf16: random signs and mantissas, exponents of [0.5, 1)
+        a = (a & 0x807F807Fu) | 0x3F003F00u;
+        b = (b & 0x807F807Fu) | 0x3F003F00u;
+      } else if constexpr (KIND == 2) {  // fp16: the same
+        a = (a & 0x83FF83FFu) | 0x38003800u;
+        b = (b & 0x83FF83FFu) | 0x38003800u;
+      } else if constexpr (KIND == 3) {  // E4M3 without the NaN codes
+        a &= 0xF7F7F7F7u;
+        b &= 0xF7F7F7F7u;
+      }
+      x[i][e] = a;
+      y[i][e] = b;
+    }
+  }
+  const uint32_t sc = 0x7C7D7E7Fu ^ (probe_hash(base) & 0x03030303u);  // E8M0 near 1
+  u32x8_t x8[KIND == 3 ? 8 : 1], y8[KIND == 3 ? 8 : 1];  // FP8 operands: 32 bytes per lane
+  if constexpr (KIND == 3) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x8[i] = u32x8_t{x[i][0], x[i][1], x[i][2], x[i][3], y[i][0], y[i][1], y[i][2], y[i][3]};
+      y8[i] = u32x8_t{y[i][0], y[i][1], y[i][2], y[i][3], x[i][0], x[i][1], x[i][2], x[i][3]};
+    }
+  }
+  f32x4_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // (the instructions exist in the device pass only: the host pass checks
+  // inline-asm operands against the host's registers)
+#if defined(__HIP_DEVICE_COMPILE__)
+  for (int64_t it = 0; it < iters; ++it) {
+    asm volatile("s_nop 4");  // the operands' last vector writes before the first product
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (KIND == 0)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+v"(c[i]) : "v"(x[i]), "v"(y[i]), "v"(sc));
+      else if constexpr (KIND == 1)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[i]) : "v"(x[i]), "v"(y[i]));
+      else if constexpr (KIND == 2)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c[i]) : "v"(x[i]), "v"(y[i]));
+      else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                     : "+v"(c[i]) : "v"(x8[i]), "v"(y8[i]), "v"(sc));
+    }
+  }
+  // the last instructions' results are read only after their passes end
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  f32x4_t t = c[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) t += c[i];
+  const uint32_t w = __float_as_uint(t[0]) ^ __float_as_uint(t[1]) ^ __float_as_uint(t[2]) ^ __float_as_uint(t[3]);
+  if (w == kProbeMagic) sink[0] = w;
+}
+
 }  // namespace
+
+int mfma_probe_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return 2 * cus;  // two workgroups of four waves per compute unit: two waves per SIMD
+}
+
+hipError_t launch_mfma_probe(int kind, int64_t iters, uint32_t seed, uint32_t* sink, int grid, hipStream_t stream) {
+  const dim3 g((unsigned)grid), b(kMfmaProbeWaves * 64);
+  switch (kind) {
+    case 0: mfma_probe_kernel<0><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    case 1: mfma_probe_kernel<1><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    case 2: mfma_probe_kernel<2><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    default: mfma_probe_kernel<3><<<g, b, 0, stream>>>(iters, seed, sink); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t nchunks = bytes / 1024;

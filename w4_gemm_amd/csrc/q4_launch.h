@@ -44,6 +44,10 @@ struct QOut {
 // Plain streaming read of `bytes` (a multiple of 1024) at src (16-byte
 // aligned); `sink` (device uint32) is never written by real data.
 hipError_t launch_read_probe(const uint8_t* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+// Workgroups the matrix-instruction probe launches on the current device
+// (0 if the device cannot be queried).
+int mfma_probe_grid();
+hipError_t launch_mfma_probe(int kind, int64_t iters, uint32_t seed, uint32_t* sink, int grid, hipStream_t stream);
 
 // Quantize bf16 src [rows][ld] into codes/scales (fmt 0 INT4 g128,
 // 1 MXFP4, 2 NVFP4; layout 0 row-major, 1 tiled).  NVFP4: gs receives the
