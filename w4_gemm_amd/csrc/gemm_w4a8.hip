@@ -177,22 +177,35 @@ w4a8_tiled_kernel(const uint8_t* __restrict__ a_codes, const float* __restrict__
     }
     i32x8_t a[2];
     a[0] = load_a(0);
-    // one A fragment in flight ahead of the products (the fences keep the
-    // compiler from hoisting every fragment load, which would not fit the
-    // register budget of two waves per SIMD)
+    // One A fragment in flight ahead of the products, and the group-scaled
+    // accumulation of row tile i done after the products of tile i+1 have
+    // been issued, so it reads results whose latency has passed instead of
+    // waiting on them (the fences keep the compiler from hoisting every
+    // fragment load, which would not fit the register budget of two waves
+    // per SIMD).
+    f32x4_t p[2][2];
+    auto scale_add = [&](int i) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][jj][r] = __builtin_fmaf(p[i & 1][jj][r], sw[jj], acc[i][jj][r]);
+    };
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i < 15) a[(i + 1) & 1] = load_a(i + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+      for (int jj = 0; jj < 2; ++jj)
+        p[i & 1][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             a[i & 1], wq[jj], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][jj][r] = __builtin_fmaf(p[r], sw[jj], acc[i][jj][r]);
+      if (i > 0) {
+        scale_add(i - 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // the two products first,
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // then the previous tile's 8 FMAs
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    scale_add(15);
   };
 
   issue_codes(0);
