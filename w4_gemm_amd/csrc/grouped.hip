@@ -143,21 +143,27 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
       const int g = p < r1 ? (gather ? gather[p] : p) : -1;
       srow[j] = (g >= 0 && g < T) ? g : 0;  // invalid rows staged from row 0, output zeroed
     }
-    u32x4_t xr[2];
-    auto load_x = [&](int st) {
+    // x(s) is held in register set s % 2 between its load and its write to
+    // LDS buffer s % 2
+    u32x4_t xr[2][2];
+    auto load_x = [&](int st, auto setc) {
+      constexpr int X = decltype(setc)::value;
       if (xw) {
         const int k = min(st, S - 1) * 128 + xk;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          xr[j] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)srow[j] * lda + k);
+          xr[X][j] = *reinterpret_cast<const u32x4_t*>(A + (int64_t)srow[j] * lda + k);
       }
     };
-    auto store_x = [&](int buf) {
+    auto store_x = [&](auto setc) {
+      constexpr int X = decltype(setc)::value;
       if (xw) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&xs[buf][xrow + 24 * j][xk]) = xr[j];
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(&xs[X][xrow + 24 * j][xk]) = xr[X][j];
       }
     };
+    using X0 = std::integral_constant<int, 0>;
+    using X1 = std::integral_constant<int, 1>;
 
     f32x4_t acc[kTPW][kBT];
 #pragma unroll
@@ -203,40 +209,51 @@ grouped_tiled_kernel(const uint16_t* __restrict__ A, int64_t lda, int T,
       }
     };
 
-    // Copy plan, per iteration st (j = st % 4): x(st+1) loads, the weight
-    // DMA of stage st+2 (kTPW per wave), and when j == 2 the scale words of
-    // group st/4 + 1 (kTPW loads, after W(st+2) = the group's first stage).
-    // At the top of iteration st, W(st) -- and at j == 0 the scales of the
-    // group -- must have landed; the copies issued after them may stay in
-    // flight: W(st+1), plus at j == 3 the scale loads issued after it.
-    // Prologue: x(0), W(0), scales(0), W(1).
-    load_x(0);
+    // Copy plan, per iteration st (J = st % 4), in issue order: the x rows of
+    // stage st+2 (two loads per thread of waves 0..5, none in waves 6, 7),
+    // the weight DMA of stage st+2 (kTPW per wave), and when J == 2 the
+    // scale words of group st/4 + 1 (kSLoads, after W(st+2) = the group's
+    // first stage).  Loads complete in order, so each wait below is the
+    // number of loads issued after the ones it needs:
+    //   * top of iteration st: W(st) -- and at J == 0 the scales issued right
+    //     after it -- have landed; x(st+1), W(st+1) (and at J == 3 the scales
+    //     after W(st+1)) may be in flight.  x(st) is in LDS (written by its
+    //     waves before their wait for lgkmcnt 0, visible after the barrier).
+    //   * after the math of stage st: x(st+1) (issued before W(st+1)) has
+    //     landed, so its waves write it to LDS; W(st+1), W(st+2) and the
+    //     x(st+2) loads stay in flight.
+    // Prologue: x(0), W(0), scales(0), x(1), W(1).
+    constexpr int kNX = 2;  // x loads per thread of a staging wave
+    load_x(0, X0());
     issue_w(0);
     issue_s(0);
+    load_x(1, X1());
     issue_w(1);
-    wait_vmcnt<2 * kTPW + kSLoads>();  // x(0) landed (W(0..2) and scales may not have)
-    store_x(0);
+    if (xw) wait_vmcnt<2 * kTPW + kSLoads + kNX>();  // x(0) landed
+    store_x(X0());
     auto iteration = [&](int st, auto jc) {
       constexpr int J = decltype(jc)::value;
-      // this wave's weight copies of stage st and its x(st) writes to LDS
-      // complete, then the barrier makes every wave's visible
-      if constexpr (J == 3) wait_vmcnt_lgkm0<kTPW + kSLoads>();
-      else wait_vmcnt_lgkm0<kTPW>();
+      constexpr int SA = J == 3 ? kSLoads : 0;  // scales issued after W(st+1)
+      constexpr int SB = J == 2 ? kSLoads : 0;  // scales issued after W(st+2)
+      if (xw) wait_vmcnt_lgkm0<kNX + kTPW + SA>();
+      else wait_vmcnt_lgkm0<kTPW + SA>();
       stage_barrier();
       if constexpr (J == 0) {
 #pragma unroll
         for (int t = 0; t < kTPW; ++t) scur[t] = snext[t];
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_x(st + 1);
+      if constexpr ((J & 1) == 0) load_x(st + 2, X0());
+      else load_x(st + 2, X1());
       issue_w(st + 2);
       if constexpr (J == 2) issue_s((st >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
       stage_math(st, jc);
-      // x(st+1) has landed once at most the copies issued after it remain
-      if constexpr (J == 2) wait_vmcnt<kTPW + kSLoads>();
-      else wait_vmcnt<kTPW>();
-      store_x((st + 1) & 1);
+      if (xw) {
+        wait_vmcnt<kTPW + SA + kNX + kTPW + SB>();
+        if constexpr ((J & 1) == 0) store_x(X1());
+        else store_x(X0());
+      }
     };
     using J0 = std::integral_constant<int, 0>;
     using J1 = std::integral_constant<int, 1>;
