@@ -30,7 +30,10 @@
 //   * one barrier per stage, before it a wait for this wave's copies of the
 //     stage (explicit vmcnt) and for all its LDS reads (lgkmcnt 0), so no
 //     wave still reads the buffer the next copies overwrite; the stage loop
-//     unrolled by four (the scheme of the W4A4 kernel in gemm_w4a4.hip);
+//     unrolled by four;
+//   * the products of a row tile go to a fresh register set and are scaled
+//     into its accumulators after the next row tile's products are issued,
+//     so the vector FMAs never wait on the matrix core's latency;
 //   * workgroups ordered so the 32 running on one XCD share A and W panels.
 // Generic kernel (any layout): one thread per output, the same promotion
 // order, for the shapes and layouts the tiled kernel does not take.

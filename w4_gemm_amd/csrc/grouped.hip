@@ -28,7 +28,8 @@
 //     stay in flight without holding registers.  Scale words (one group of
 //     four stages) are loaded into registers ahead of their group.  The
 //     chunk's activation rows for a stage (48 x 128 bf16) are gathered into
-//     LDS through registers by waves 0..5 (two buffers).
+//     LDS through registers by waves 0..5 (two LDS buffers), loaded two
+//     stages ahead into two register sets.
 //   * one barrier per stage; every wait is an explicit vmcnt count (the
 //     stage loop is unrolled by four so each count is a constant).
 //   * matrix step i of a super-chunk uses codes 8i..8i+8 of every lane of a
