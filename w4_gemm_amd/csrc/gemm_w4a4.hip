@@ -13,9 +13,7 @@
 // Work decomposition:
 //   * a workgroup of 8 waves computes a 256 x 256 block of C; wave (wm, wn),
 //     wm in 0..1, wn in 0..3, owns 128 x 64 = 8 x 4 matrix-core tiles (128
-//     fp32 accumulators per lane).  The scaled MFMA has no form whose result
-//     register is its accumulator input, so the accumulators must leave room
-//     for a free destination: 256 per lane would fill the accumulator file.
+//     fp32 accumulators per lane, two waves per SIMD).
 //   * K advances in stages of one super-chunk (128 k).  A stage needs 16
 //     A tiles and 16 W tiles (32 KB); they are copied verbatim into LDS by
 //     direct global->LDS loads (global_load_lds_dwordx4: one 1 KB tile per
@@ -24,15 +22,11 @@
 //     Scales are copied per group of four stages (16 x 256 B for each
 //     operand) into two buffers.  Every fragment read from LDS is one
 //     contiguous kilobyte (conflict-free).
-//   * one barrier per stage: each wave first waits for its own copies of
-//     the next stage (explicit vmcnt); the barrier then makes every wave's
-//     copies visible.  The copies issued after it overwrite the buffer of
-//     the stage before the current one, whose fragments every wave read
-//     during the stage before that and consumed in the matrix instructions
-//     of the previous stage -- before this barrier in program order -- so
-//     no wave still reads it, and no wave has to drain its LDS reads before
-//     the barrier.  The stage loop is unrolled by four so each wait count
-//     is a constant.
+//   * ping-pong schedule: the two waves of each SIMD alternate a memory step
+//     (the stage's 12 fragment reads into registers) and a matrix step (its
+//     32 products), half a stage apart, with a barrier between phases; the
+//     matrix core of every SIMD is fed by one wave while the other reads.
+//     The rules that make the LDS reuse safe are stated at the loop.
 //   * workgroups are ordered so that the 32 running on one XCD cover a
 //     4 x 8 block of C (shared A and W panels stay in that XCD's L2).
 //   * the weight is the matrix instruction's row operand (C^T = W' A'^T per
@@ -125,112 +119,89 @@ w4a4_tiled_kernel(const uint8_t* __restrict__ a_codes, const uint8_t* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Fragments in registers: the A fragments of the stage being multiplied
-  // (each reloaded with the next stage's as soon as its four products are
-  // issued), the W fragments of two stages (alternating), the scale words
-  // of the current and the next group of four stages (byte s % 4 of each is
-  // the stage's E8M0, picked by the matrix instruction's op_sel).
-  u32x4_t a[8], w[2][4];
-  uint32_t sa[8], sw[4], san[8], swn[4];
-  auto read_scales = [&](int t, uint32_t (&xa)[8], uint32_t (&xw)[4]) {
-    const uint8_t(*sb)[256] = sbuf[(t >> 2) & 1];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + i][lane * 4]);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) xw[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
-  };
-  auto read_w = [&](int t, u32x4_t (&dst)[4]) {
-    const uint8_t(*cb)[1024] = cbuf[t % kCodeBufs];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dst[jj] = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + jj][lane * 16]);
-  };
-  auto read_a = [&](int t, int i) {
-    return *reinterpret_cast<const u32x4_t*>(&cbuf[t % kCodeBufs][wm * 8 + i][lane * 16]);
-  };
+  // Fragments of the stage a wave multiplies, in registers (one set), and
+  // the scale words of the current group of four stages (byte s % 4 of each
+  // is stage s's E8M0, picked by the matrix instruction's op_sel).
+  u32x4_t a[8], w[4];
+  uint32_t sa[8], sw[4];
   auto as8 = [](u32x4_t v) { return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0}; };
-
-  // Iteration s (J = s % 4): wait until only copy group s+2 may be
-  // outstanding (group s+1 has landed), barrier, then multiply stage s from
-  // registers while reading stage s+1's fragments: after the four products
-  // of A fragment i, its successor, and for i < 4 also W fragment i of the
-  // next stage (the other register set); after the products of A fragment 0
-  // the copies of group s+3 (into the buffer of stage s-1); when J == 3,
-  // after A fragments 4..6, the next group's scale words.  Reading the next
-  // stage's W fragments after the first products rather than before them
-  // keeps every fragment a product needs at most 11 LDS reads back, so its
-  // wait is a count, not a drain of the reads just issued.  Copies in group
-  // t: kCopies, plus the scale copy when t % 4 == 0.  (Past the last stage
-  // the reads fetch a buffer holding a clamped copy of the last stage: in
-  // bounds, never used.)
-  auto iteration = [&](int s, auto jc) {
+  // memory step of stage u: its fragments (and at J == 0 its group's scale
+  // words) from LDS into registers
+  auto load = [&](int u, auto jc) {
     constexpr int J = decltype(jc)::value;
-    constexpr int P = J & 1;
-    if constexpr (J == 2) wait_vmcnt<kCopies + 1>();
-    else wait_vmcnt<kCopies>();
-    stage_barrier();
-    const uint8_t(*cb)[1024] = cbuf[(s + 1) % kCodeBufs];
-    const uint8_t(*sb)[256] = sbuf[((s + 1) >> 2) & 1];
+    const uint8_t(*cb)[1024] = cbuf[u % kCodeBufs];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) w[jj] = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + jj][lane * 16]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(&cb[wm * 8 + i][lane * 16]);
+    if constexpr (J == 0) {
+      const uint8_t(*sb)[256] = sbuf[(u >> 2) & 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + i][lane * 4]);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sw[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
+    }
+  };
+  // matrix step of stage u: its 32 products, with this wave's part of copy
+  // group u+3 issued after the first four (into the buffer of stage u-1)
+  auto compute = [&](int u, auto jc) {
+    constexpr int J = decltype(jc)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as8(w[P][jj]), as8(a[i]), acc[i][jj], 4, 4,
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as8(w[jj]), as8(a[i]), acc[i][jj], 4, 4,
                                                                       J, sw[jj], J, sa[i]);
-      a[i] = *reinterpret_cast<const u32x4_t*>(&cb[wm * 8 + i][lane * 16]);
-      if (i < 4) w[P ^ 1][i] = *reinterpret_cast<const u32x4_t*>(&cb[kBM + wn * 4 + i][lane * 16]);
-      if constexpr (J == 3) {
-        if (i == 4 || i == 5) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            san[4 * (i - 4) + r] = *reinterpret_cast<const uint32_t*>(&sb[wm * 8 + 4 * (i - 4) + r][lane * 4]);
-        }
-        if (i == 6) {
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) swn[jj] = *reinterpret_cast<const uint32_t*>(&sb[kBM + wn * 4 + jj][lane * 4]);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // the four products of A fragment i
       if (i == 0) {
-        issue_codes(s + 3);
-        if constexpr (J == 1) issue_scales(s + 3);
-        __builtin_amdgcn_sched_group_barrier(0x020, kCopies + (J == 1 ? 1 : 0), 0);
+        issue_codes(u + 3);
+        if constexpr (J == 1) issue_scales(u + 3);
       }
-      // then the LDS reads issued above
-      if (i < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      else if (J == 3 && i < 7) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (J == 3) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sa[i] = san[i];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sw[jj] = swn[jj];
     }
   };
 
-  // prologue: copy groups 0 (codes + scales), 1 and 2; stage 0 into registers
+  // Ping-pong: the waves of each SIMD (w and w+4) alternate a memory step
+  // and a matrix step, so that the matrix core of every SIMD is fed by one
+  // wave while the other reads its next fragments.  Every wave runs
+  //   load(u) -> wait -> barrier -> compute(u) -> barrier
+  // and waves 4..7 start one barrier later: in phase 2u waves 0..3 multiply
+  // stage u while waves 4..7 load it, in phase 2u+1 the reverse (waves 0..3
+  // loading stage u+1).  The wait at the end of load(u): this wave's LDS
+  // reads (its next matrix step needs them) and its part of copy group u+1
+  // (only group u+2 may still be in flight).  Stage u+1 is then visible after
+  // the barrier that ends load(u) of waves 4..7, before any wave reads it;
+  // and copy group u+3 (issued in compute(u), phase 2u or 2u+1) overwrites
+  // stage u-1's buffer, whose last reads (load(u-1) of waves 4..7, phase
+  // 2u-2) completed before the barrier ending that phase.  Copies in group
+  // t: kCopies, plus the scale copy when t % 4 == 0.  (Past the last stage
+  // the copies repeat the last stage into free buffers and the last loads
+  // read them: in bounds, never used.)
   issue_codes(0);
   issue_scales(0);
   issue_codes(1);
   issue_codes(2);
-  wait_vmcnt_lgkm0<2 * kCopies>();
+  wait_vmcnt_lgkm0<0>();
   stage_barrier();
-  read_scales(0, sa, sw);
-  read_w(0, w[0]);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = read_a(0, i);
-
+  if (wm == 1) stage_barrier();
+  auto stage = [&](int u, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    load(u, jc);
+    wait_vmcnt_lgkm0<kCopies + (J == 2 ? 1 : 0)>();  // group u+2 carries scales when J == 2
+    stage_barrier();
+    compute(u, jc);
+    stage_barrier();
+  };
   // The tiled layout has K % 512 == 0, so S is a multiple of 4.
   using J0 = std::integral_constant<int, 0>;
   using J1 = std::integral_constant<int, 1>;
   using J2 = std::integral_constant<int, 2>;
   using J3 = std::integral_constant<int, 3>;
   for (int s0 = 0; s0 < S; s0 += 4) {
-    iteration(s0, J0());
-    iteration(s0 + 1, J1());
-    iteration(s0 + 2, J2());
-    iteration(s0 + 3, J3());
+    stage(s0, J0());
+    stage(s0 + 1, J1());
+    stage(s0 + 2, J2());
+    stage(s0 + 3, J3());
   }
+  if (wm == 0) stage_barrier();  // every wave has passed the same number of barriers
   wait_vmcnt<0>();
 
   // lane l, register r of tile (i, jj) holds row 16i + l%16, column
