@@ -125,8 +125,8 @@ def mfma_ceiling(torch, q4, dev, kind):
     below the published dense peak.  Measured once per kind, after a short
     idle gap, over about 0.2 s of back-to-back launches."""
     if kind not in _MFMA_CEILING:
-        sink = torch.zeros(1, dtype=torch.int32, device=dev)
-        iters = 4096 if kind in ("fp4", "fp8") else 8192
+        sink = torch.zeros(q4.PROBE_MIX_SINK if kind.startswith("fp4_") else 1, dtype=torch.int32, device=dev)
+        iters = 4096 if kind.startswith("fp4") or kind == "fp8" else 8192
         flops = [0.0]
 
         def fn():
@@ -139,13 +139,13 @@ def mfma_ceiling(torch, q4, dev, kind):
     return _MFMA_CEILING[kind]
 
 
-def with_ceiling(res, torch, q4, dev, kind, keys=("TFLOPs",)):
+def with_ceiling(res, torch, q4, dev, kind, keys=("TFLOPs",), prefix="mfma_ceiling"):
     """Adds the measured ceiling of `kind` and each rate's fraction of it."""
     c = mfma_ceiling(torch, q4, dev, kind)
-    res["mfma_ceiling_TFLOPs"] = round(c, 1)
-    res["mfma_ceiling_kind"] = kind
+    res[f"{prefix}_TFLOPs"] = round(c, 1)
+    res[f"{prefix}_kind"] = kind
     for k in keys:
-        res["frac_mfma_ceiling" if k == "TFLOPs" else f"frac_mfma_ceiling_{k}"] = round(res[k] / c, 4)
+        res[f"frac_{prefix}" if k == "TFLOPs" else f"frac_{prefix}_{k}"] = round(res[k] / c, 4)
     return res
 
 
@@ -370,8 +370,12 @@ def main():
     if _MFMA_CEILING:
         extra["mfma_ceilings_TFLOPs"] = {
             k: {"measured": round(v, 1), "published_peak": {"fp4": FP4_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS,
-                                                          "fp16": FP16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS}[k],
-                "note": "random register operands, q4_mfma_probe"}
+                                                          "fp16": FP16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS,
+                                                          "fp4_copy": FP4_PEAK_TFLOPS, "fp4_mix": FP4_PEAK_TFLOPS}[k],
+                "note": "random register operands, q4_mfma_probe" + (
+                    "; with the tiled W4A4 kernel's global->LDS copies" + (" and LDS fragment reads"
+                                                                           if k == "fp4_mix" else "")
+                    + " per 64 products per SIMD" if k.startswith("fp4_") else "")}
             for k, v in _MFMA_CEILING.items()}
 
     cpu = None
@@ -555,6 +559,9 @@ def bench_w4a4(torch, q4, workloads, dev, seed, fmt="mxfp4"):
         res["layer_with_fused_act_quantize_us"] = round(fms * 1e3, 1)
         res["fused_epilogue_saves_us"] = round((ums - fms) * 1e3, 1)
         res["fused_TFLOPs"] = round(2.0 * M * N * K / (fms * 1e-3) / 1e12, 1)
+        # the FP4 instruction alone, and with the kernel's copies and LDS
+        # fragment reads mixed in at its rate (what its loop can approach)
+        with_ceiling(res, torch, q4, dev, "fp4_mix", ("TFLOPs", "fused_TFLOPs"), prefix="mix_ceiling")
         return with_ceiling(res, torch, q4, dev, "fp4", ("TFLOPs", "fused_TFLOPs"))
     return with_ceiling(res, torch, q4, dev, "fp16")
 

@@ -356,12 +356,22 @@ q4_status q4_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* st
  *          Q4_PROBE_BF16 16x16x32 bf16 (GEMV, W4A16 GEMM, grouped GEMM)
  *          Q4_PROBE_F16  16x16x32 fp16 (the NVFP4 W4A4 GEMM)
  *          Q4_PROBE_FP8  scaled 16x16x128 with E4M3 operands (W4A8)
+ *          Q4_PROBE_FP4_COPY  the FP4 instruction with one direct
+ *                        global->LDS copy (1 KB per wave) issued per 8
+ *                        instructions: the copy rate per SIMD of the tiled
+ *                        W4A4 kernel
+ *          Q4_PROBE_FP4_MIX   the same plus three 16-byte-per-lane LDS
+ *                        fragment reads per 8 instructions: that kernel's
+ *                        whole memory-instruction mix, so the rate its loop
+ *                        can approach on this part
  *          other values: Q4_ERR_FORMAT
  *   iters  iterations of 8 instructions per wave, 0 .. 2^24 (else
  *          Q4_ERR_SHAPE); the launch runs two waves per SIMD on every
  *          compute unit; iters == 0 is a no-op (*flops = 0)
- *   sink   device uint32[1], written only if the folded sums equal one
- *          fixed constant (which keeps the products alive)
+ *   sink   device uint32[1] (the two FP4 mix kinds: 16384 uint32, 16-byte
+ *          aligned, else Q4_ERR_ALIGN -- the 64 KB the copies read; their
+ *          contents do not matter), written only if the folded sums equal
+ *          one fixed constant (which keeps the products alive)
  *   flops  host double: receives the floating-point operations the launch
  *          performs (2*16*16*K per instruction); NULL: Q4_ERR_NULL
  */
@@ -369,7 +379,9 @@ typedef enum q4_probe_kind {
     Q4_PROBE_FP4 = 0,
     Q4_PROBE_BF16 = 1,
     Q4_PROBE_F16 = 2,
-    Q4_PROBE_FP8 = 3
+    Q4_PROBE_FP8 = 3,
+    Q4_PROBE_FP4_COPY = 4,
+    Q4_PROBE_FP4_MIX = 5
 } q4_probe_kind;
 
 q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* sink, double* flops,

@@ -151,3 +151,5 @@ def test_mfma_probe_rejects():
     _raises("iters must be an int", q4.q4_mfma_probe, "fp4", 1.5, sink)
     _raises("sink must be a torch.int32", q4.q4_mfma_probe, "fp4", 16, sink.float())
     _raises("must be a GPU tensor", q4.q4_mfma_probe, "bf16", 16, sink)
+    _raises("sink must be contiguous with at least 16384 entries", q4.q4_mfma_probe, "fp4_mix", 16, sink)
+    _raises("sink must be contiguous with at least 16384 entries", q4.q4_mfma_probe, "fp4_copy", 16, sink)

@@ -23,15 +23,18 @@ def test_read_probe_reads_and_leaves_sink():
         assert int(sink.item()) == 7
 
 
-@pytest.mark.parametrize("kind,peak", [("fp4", 10100.0), ("bf16", 2500.0), ("fp16", 2500.0), ("fp8", 5000.0)])
+@pytest.mark.parametrize("kind,peak", [("fp4", 10100.0), ("bf16", 2500.0), ("fp16", 2500.0), ("fp8", 5000.0),
+                                       ("fp4_copy", 10100.0), ("fp4_mix", 10100.0)])
 def test_mfma_probe_rate(kind, peak):
     """The probe reports its operation count, leaves the sink alone, and
     runs at a positive rate no higher than the published dense peak (plus
-    timing slack)."""
-    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    timing slack).  The two FP4 instruction-mix kinds read a 64 KB window
+    at the sink."""
+    n = q4.PROBE_MIX_SINK if kind.startswith("fp4_") else 1
+    sink = torch.full((n,), 7, dtype=torch.int32, device=DEV)
     iters = 512
     flops = q4.q4_mfma_probe(kind, iters, sink)
-    per = 2 * 16 * 16 * (128 if kind in ("fp4", "fp8") else 32)
+    per = 2 * 16 * 16 * (128 if kind.startswith("fp4") or kind == "fp8" else 32)
     waves = flops / (iters * 8 * per)
     assert waves == int(waves) and int(waves) % 8 == 0 and waves > 0
     torch.cuda.synchronize()
@@ -44,5 +47,5 @@ def test_mfma_probe_rate(kind, peak):
     tflops = 5 * flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
     print(f"{kind}: {tflops:.0f} TFLOP/s", flush=True)
     assert 0 < tflops < 1.05 * peak
-    assert int(sink.item()) == 7
+    assert torch.all(sink == 7)
     assert q4.q4_mfma_probe(kind, 0, sink) == 0.0

@@ -22,7 +22,7 @@ __all__ = [
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
     "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
-    "moe_layer", "interleave_gate_up", "q4_read_probe", "q4_mfma_probe", "PROBE_KINDS",
+    "moe_layer", "interleave_gate_up", "q4_read_probe", "q4_mfma_probe", "PROBE_KINDS", "PROBE_MIX_SINK",
     "empty_q4", "quantize", "LIB_PATH",
 ]
 
@@ -482,18 +482,22 @@ def q4_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _check(lib().q4_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "q4_read_probe")
 
 
-PROBE_KINDS = {"fp4": 0, "bf16": 1, "fp16": 2, "fp8": 3}
+PROBE_KINDS = {"fp4": 0, "bf16": 1, "fp16": 2, "fp8": 3, "fp4_copy": 4, "fp4_mix": 5}
+PROBE_MIX_SINK = 16384   # int32 entries the "fp4_copy" / "fp4_mix" kinds read (64 KB)
 
 
 def q4_mfma_probe(kind: str, iters: int, sink: torch.Tensor, seed: int = 1, stream=None) -> float:
     """Measurement helper: back-to-back matrix instructions of one kind
-    ("fp4", "bf16", "fp16", "fp8") on random register operands; returns the
-    launch's floating-point operations (sink: int32 GPU tensor [1])."""
+    ("fp4", "bf16", "fp16", "fp8") on random register operands, or the FP4
+    instruction with the tiled W4A4 kernel's global->LDS copies
+    ("fp4_copy") or its copies and LDS fragment reads ("fp4_mix") mixed in;
+    returns the launch's floating-point operations.  sink: int32 GPU tensor
+    [1] ([PROBE_MIX_SINK], 16-byte aligned, for the two mix kinds)."""
     if kind not in PROBE_KINDS:
         raise ValueError(f"kind must be one of {sorted(PROBE_KINDS)}")
     if not isinstance(iters, int) or iters < 0 or iters > (1 << 24):
         raise ValueError("iters must be an int in [0, 2^24]")
-    _vector(sink, "sink", torch.int32, 1)
+    _vector(sink, "sink", torch.int32, PROBE_MIX_SINK if PROBE_KINDS[kind] >= 4 else 1)
     _on_gpu(("sink", sink))
     flops = ctypes.c_double(0.0)
     _check(lib().q4_mfma_probe(PROBE_KINDS[kind], iters, seed & 0xFFFFFFFF, _ptr(sink), ctypes.byref(flops),

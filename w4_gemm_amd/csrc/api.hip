@@ -364,13 +364,14 @@ q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, co
 
 q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* sink, double* flops,
                         void* stream) {
-  if (kind < Q4_PROBE_FP4 || kind > Q4_PROBE_FP8) return Q4_ERR_FORMAT;
+  if (kind < Q4_PROBE_FP4 || kind > Q4_PROBE_FP4_MIX) return Q4_ERR_FORMAT;
   if (iters < 0 || iters > ((int64_t)1 << 24)) return Q4_ERR_SHAPE;
   if (!flops) return Q4_ERR_NULL;
   *flops = 0.0;
   if (iters == 0) return Q4_OK;
   if (!sink) return Q4_ERR_NULL;
-  if (!aligned(sink, 4)) return Q4_ERR_ALIGN;
+  // the instruction-mix kinds copy 16 bytes per lane from the sink window
+  if (!aligned(sink, kind >= Q4_PROBE_FP4_COPY ? 16 : 4)) return Q4_ERR_ALIGN;
   const int grid = q4::mfma_probe_grid();
   if (grid <= 0) return hip_status(hipErrorInvalidDevice);
   const double per = (kind == Q4_PROBE_BF16 || kind == Q4_PROBE_F16) ? 2.0 * 16 * 16 * 32 : 2.0 * 16 * 16 * 128;

@@ -24,8 +24,20 @@
 // (each accumulator is reused 8 instructions later), two waves per SIMD.
 // The instructions are written out so that every accumulator stays in
 // place: nothing else runs in the loop.
+//
+// Two more kinds run the FP4 instruction at the same rate with the memory
+// instructions of the tiled W4A4 kernel mixed in, per SIMD and 64
+// instructions: 8 direct global->LDS copies of 1 KB (kind 4), and those
+// plus 24 LDS fragment reads of 16 bytes per lane (kind 5) -- what that
+// kernel issues per stage.  The copies read a 64 KB window at the sink
+// pointer (L2-resident), each wave into its own ring of four 1 KB LDS
+// slots; the reads take a wave's own 4 KB of LDS.  The difference to kind
+// 0 is what those instructions cost the matrix core (issue slots, and the
+// clock, which power sets).
 #include "q4_launch.h"
 #include "q4_mma.h"
+
+#include <type_traits>
 
 namespace q4 {
 namespace {
@@ -67,11 +79,16 @@ __device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
   return x;
 }
 
-// KIND: 0 FP4 16x16x128 (scaled), 1 bf16 16x16x32, 2 fp16 16x16x32, 3 FP8 16x16x128 (scaled)
+// KIND: 0 FP4 16x16x128 (scaled), 1 bf16 16x16x32, 2 fp16 16x16x32, 3 FP8 16x16x128 (scaled),
+// 4 FP4 with one copy per 8 instructions, 5 FP4 with one copy and three fragment reads per 8
 template <int KIND>
 __global__ void __launch_bounds__(kMfmaProbeWaves * 64)
 mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
+  constexpr bool kCopy = KIND >= 4, kRead = KIND == 5;
+  // per wave: four 1 KB copy slots, then 4 KB of fragments to read
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kCopy ? kMfmaProbeWaves * 8192 : 16];
   const uint32_t base = (seed * 0x9E3779B1u) ^ ((blockIdx.x * blockDim.x + threadIdx.x) * 64u);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   u32x4_t x[8], y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -106,12 +123,38 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
   for (int i = 0; i < 8; ++i) c[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // (the instructions exist in the device pass only: the host pass checks
   // inline-asm operands against the host's registers)
+  uint8_t* const ring = lds + (kCopy ? wave * 8192 : 0);
+  const uint8_t* const csrc = reinterpret_cast<const uint8_t*>(sink) + lane * 16;
+  const int cbase = blockIdx.x * kMfmaProbeWaves + wave;
+  u32x4_t r[2][3] = {};
+  if constexpr (kRead) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) reinterpret_cast<uint32_t*>(ring + 4096)[lane + 64 * j] = probe_hash(base + 977u * j);
+  }
 #if defined(__HIP_DEVICE_COMPILE__)
-  for (int64_t it = 0; it < iters; ++it) {
+  const uint32_t fra = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(ring + 4096) + lane * 16;
+  auto iteration = [&](int64_t it, auto set) {
+    constexpr int R = decltype(set)::value;  // register set of this iteration's fragment reads
     asm volatile("s_nop 4");  // the operands' last vector writes before the first product
+    if constexpr (kRead)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[R ^ 1][0]), "+v"(r[R ^ 1][1]), "+v"(r[R ^ 1][2]) :: "memory");
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if constexpr (KIND == 0)
+      if constexpr (kCopy) {
+        if (i == 1)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(csrc + ((cbase + it) & 63) * 1024),
+                                           (__attribute__((address_space(3))) void*)(ring + (it & 3) * 1024), 16, 0, 0);
+      }
+      if constexpr (kRead) {
+        // three 16-byte reads early in each iteration into register set R;
+        // the next iteration starts by waiting for them (long landed) and
+        // taking them as read, so their registers stay theirs until then
+        if (i < 3) {
+          const uint32_t addr = fra + (uint32_t)(((it + i) & 3) * 1024);
+          asm volatile("ds_read_b128 %0, %1" : "=v"(r[R][i]) : "v"(addr) : "memory");
+        }
+      }
+      if constexpr (KIND == 0 || KIND >= 4)
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
                      : "+v"(c[i]) : "v"(x[i]), "v"(y[i]), "v"(sc));
       else if constexpr (KIND == 1)
@@ -122,14 +165,28 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
                      : "+v"(c[i]) : "v"(x8[i]), "v"(y8[i]), "v"(sc));
     }
+    if constexpr (kCopy) __builtin_amdgcn_s_waitcnt((1 & 0xF) | (0x7 << 4) | (0xF << 8));  // vmcnt(1): one copy in flight
+  };
+  int64_t it = 0;
+  for (; it + 1 < iters; it += 2) {
+    iteration(it, std::integral_constant<int, 0>());
+    iteration(it + 1, std::integral_constant<int, 1>());
   }
+  if (it < iters) iteration(it, std::integral_constant<int, 0>());
   // the last instructions' results are read only after their passes end
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #endif
   f32x4_t t = c[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) t += c[i];
-  const uint32_t w = __float_as_uint(t[0]) ^ __float_as_uint(t[1]) ^ __float_as_uint(t[2]) ^ __float_as_uint(t[3]);
+  uint32_t w = __float_as_uint(t[0]) ^ __float_as_uint(t[1]) ^ __float_as_uint(t[2]) ^ __float_as_uint(t[3]);
+  if constexpr (kRead) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) w ^= r[s][j][0] ^ r[s][j][1] ^ r[s][j][2] ^ r[s][j][3];
+  }
+  if constexpr (kCopy) w ^= reinterpret_cast<const uint32_t*>(ring)[lane];
   if (w == kProbeMagic) sink[0] = w;
 }
 
@@ -148,7 +205,9 @@ hipError_t launch_mfma_probe(int kind, int64_t iters, uint32_t seed, uint32_t* s
     case 0: mfma_probe_kernel<0><<<g, b, 0, stream>>>(iters, seed, sink); break;
     case 1: mfma_probe_kernel<1><<<g, b, 0, stream>>>(iters, seed, sink); break;
     case 2: mfma_probe_kernel<2><<<g, b, 0, stream>>>(iters, seed, sink); break;
-    default: mfma_probe_kernel<3><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    case 3: mfma_probe_kernel<3><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    case 4: mfma_probe_kernel<4><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    default: mfma_probe_kernel<5><<<g, b, 0, stream>>>(iters, seed, sink); break;
   }
   return hipGetLastError();
 }
