@@ -214,7 +214,7 @@ def test_quantize_strided_source_and_empty():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("layout,rows,cols", [("rows", 96, 768), ("tiled", 90, 1024)])
+@pytest.mark.parametrize("layout,rows,cols", [("rows", 96, 768), ("rows", 97, 896), ("tiled", 90, 1024)])
 def test_dequant_bit_exact(fmt, layout, rows, cols):
     w = workloads.matrix(f"tq/dq{cols}", rows, cols, 0.03, seed=15, outlier_frac=0.01,
                          outlier_mult=30.0)

@@ -390,31 +390,48 @@ __global__ void set_word_kernel(uint32_t* p, uint32_t v) { *p = v; }
 // which multiplies the E2M1 value by the power of two exactly -- the same
 // bits; other blocks take the plain path.  NVFP4 reads its E2M1 values
 // through the same instruction with scale 1 (exact) before the multiply.
-template <int FMT, int OUT, int LAYOUT>
-__device__ __forceinline__ void dequant8(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
-                                         float gs, int64_t r, int64_t k0, int64_t cols, void* __restrict__ dst,
-                                         int64_t ld) {
-  const uint32_t packed = *reinterpret_cast<const uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols));
+// Split in two so that a lane can issue the loads of several chunks before
+// it converts the first: dq_load fetches the 8 codes and the raw scale
+// field, dq_store converts and writes them.
+struct DqIn {
+  uint32_t packed;  // 8 codes, element j in nibble j
+  uint32_t sraw;    // the scale field as stored (fp16 bits, E8M0, E4M3, or the INT4-zp word)
+};
+
+template <int FMT, int LAYOUT>
+__device__ __forceinline__ DqIn dq_load(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                        int64_t r, int64_t k0, int64_t cols) {
+  DqIn d;
+  d.packed = *reinterpret_cast<const uint32_t*>(codes + code_off8<LAYOUT>(r, k0, cols));
   const int64_t si = scale_off<FMT, LAYOUT>(r, k0, cols);
+  if constexpr (FMT == 0) d.sraw = reinterpret_cast<const uint16_t*>(scales)[si];
+  else if constexpr (FMT == 4) d.sraw = reinterpret_cast<const uint32_t*>(scales)[si];
+  else d.sraw = reinterpret_cast<const uint8_t*>(scales)[si];
+  return d;
+}
+
+template <int FMT, int OUT>
+__device__ __forceinline__ void dq_store(DqIn d, float gs, int64_t r, int64_t k0, void* __restrict__ dst,
+                                         int64_t ld) {
+  const uint32_t packed = d.packed;
   float v[8];
   if constexpr (FMT == 0) {
-    const float s = fp16_value(reinterpret_cast<const uint16_t*>(scales)[si]);
+    const float s = fp16_value(d.sraw);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int q = ((int)(packed << (28 - 4 * j))) >> 28;  // sign-extend nibble j
       v[j] = (float)q * s;
     }
   } else if constexpr (FMT == 4) {
-    const uint32_t word = reinterpret_cast<const uint32_t*>(scales)[si];
-    const float s = fp16_value(word & 0xFFFFu);
-    const int z = (int)(int8_t)((word >> 16) & 0xFFu);
+    const float s = fp16_value(d.sraw & 0xFFFFu);
+    const int z = (int)(int8_t)((d.sraw >> 16) & 0xFFu);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int q = ((int)(packed << (28 - 4 * j))) >> 28;
       v[j] = (float)(q - z) * s;
     }
   } else if constexpr (FMT == 1) {
-    const uint32_t e = reinterpret_cast<const uint8_t*>(scales)[si];
+    const uint32_t e = d.sraw;
     const float s = e8m0_value(e);
     if (e >= 2u && e <= 252u) {
       if constexpr (OUT == 0) {
@@ -438,7 +455,7 @@ __device__ __forceinline__ void dequant8(const uint8_t* __restrict__ codes, cons
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = e2m1_value((packed >> (4 * j)) & 0xFu) * s;
   } else {
-    const float eff = e4m3_value(reinterpret_cast<const uint8_t*>(scales)[si]) * gs;
+    const float eff = e4m3_value(d.sraw) * gs;
     const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 0);
     const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 1);
     const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, 2);
@@ -460,8 +477,14 @@ __device__ __forceinline__ void dequant8(const uint8_t* __restrict__ codes, cons
   }
 }
 
-// One lane per 8 values over the flattened chunks; IDX32: the chunk count
-// fits 32 bits, so the row comes from a 32-bit division.
+// Dequantization walks the flattened chunks of 8 values.  Each lane takes
+// kDqUnroll chunks a grid-stride apart (so that each wave instruction still
+// covers consecutive chunks: 1 KB of bf16 per store) and issues all their
+// loads before converting the first: decode is bound by the latency of
+// those small loads otherwise.  IDX32: the chunk count fits 32 bits, so
+// the row comes from a 32-bit division.
+constexpr int kDqUnroll = 4;
+
 template <int FMT, int OUT, int LAYOUT, bool IDX32>
 __global__ void __launch_bounds__(kThreads)
 dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
@@ -470,10 +493,80 @@ dequant_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scale
   const int64_t cpr = cols >> 3;
   const int64_t total = rows * cpr;
   const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
-       c += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = IDX32 ? (int64_t)((uint32_t)c / (uint32_t)cpr) : c / cpr;
-    dequant8<FMT, OUT, LAYOUT>(codes, scales, gs, r, (c - r * cpr) * 8, cols, dst, ld);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < total; c0 += kDqUnroll * stride) {
+    DqIn d[kDqUnroll];
+    int64_t rr[kDqUnroll], kk[kDqUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const int64_t c = min(c0 + u * stride, total - 1);  // past the end: load the last chunk again
+      rr[u] = IDX32 ? (int64_t)((uint32_t)c / (uint32_t)cpr) : c / cpr;
+      kk[u] = (c - rr[u] * cpr) * 8;
+      d[u] = dq_load<FMT, LAYOUT>(codes, scales, rr[u], kk[u], cols);
+    }
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u)
+      if (c0 + u * stride < total) dq_store<FMT, OUT>(d[u], gs, rr[u], kk[u], dst, ld);
+  }
+}
+
+// Tiled layout: a wave takes 16 rows x 512 k (four 1 KB tiles, one scale
+// group) -- four whole-kilobyte loads and one load of the group's scale
+// bytes -- and stages them in its own LDS space; it then walks the 16 rows,
+// lane l converting the 8 codes at k = 8l of the row (4 bytes of LDS) and
+// storing them as one 16-byte piece of a contiguous kilobyte of the row, so
+// both the reads and the writes are whole kilobytes.
+constexpr int kDqtWaves = kThreads / 64;
+
+template <int FMT>
+struct DqtScales {  // the scale group of one 16-row tile and 512 k, as stored
+  static constexpr int kBytes = FMT == 0 ? 128 : FMT == 2 ? 512 : 256;
+  static constexpr int kPerLane = kBytes / 64;  // 2, 4 or 8 bytes
+};
+
+template <int FMT, int OUT>
+__global__ void __launch_bounds__(kThreads)
+dequant_tiled_kernel(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                     const float* gs_ptr, int64_t rows, int64_t cols, void* __restrict__ dst,
+                     int64_t ld) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kDqtWaves][4096 + 512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t S = cols >> 7, Q = cols >> 9;
+  const int64_t units = ((rows + 15) >> 4) * Q;
+  const int64_t unit = (int64_t)blockIdx.x * kDqtWaves + wave;
+  if (unit >= units) return;  // wave-uniform; no barrier follows
+  const float gs = (FMT == 2) ? *gs_ptr : 0.0f;
+  const int64_t t = unit / Q, q = unit - t * Q;
+  uint8_t* const sc = stage[wave];
+  // four tiles (t, 4q .. 4q+3): 1 KB each
+  const uint8_t* const tsrc = codes + ((t * S + 4 * q) << 10) + lane * 16;
+  uint4 w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = *reinterpret_cast<const uint4*>(tsrc + j * 1024);
+  const uint8_t* const ssrc = reinterpret_cast<const uint8_t*>(scales) +
+                              (t * Q + q) * DqtScales<FMT>::kBytes + lane * DqtScales<FMT>::kPerLane;
+  if constexpr (DqtScales<FMT>::kPerLane == 2)
+    *reinterpret_cast<uint16_t*>(sc + 4096 + lane * 2) = *reinterpret_cast<const uint16_t*>(ssrc);
+  else if constexpr (DqtScales<FMT>::kPerLane == 4)
+    *reinterpret_cast<uint32_t*>(sc + 4096 + lane * 4) = *reinterpret_cast<const uint32_t*>(ssrc);
+  else
+    *reinterpret_cast<uint2*>(sc + 4096 + lane * 8) = *reinterpret_cast<const uint2*>(ssrc);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(sc + j * 1024 + lane * 16) = w[j];
+  __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads (one wave, in order)
+  // lane l: k = 8l of the 512, i.e. tile s = l/16, 32-k group g = (l/4)%4, piece p = l%4
+  const int s = lane >> 4, g = (lane >> 2) & 3, pc = lane & 3;
+  const int64_t k0 = 512 * q + 8 * lane;
+  const int nrows = (int)min((int64_t)16, rows - 16 * t);
+  for (int n = 0; n < nrows; ++n) {
+    const int tl = g * 16 + n;  // the lane of the tile that holds these codes
+    DqIn d;
+    d.packed = *reinterpret_cast<const uint32_t*>(sc + s * 1024 + tl * 16 + pc * 4);
+    if constexpr (FMT == 0) d.sraw = *reinterpret_cast<const uint16_t*>(sc + 4096 + (n * 4 + s) * 2);
+    else if constexpr (FMT == 4) d.sraw = *reinterpret_cast<const uint32_t*>(sc + 4096 + (n * 4 + s) * 4);
+    else if constexpr (FMT == 1) d.sraw = sc[4096 + tl * 4 + s];
+    else d.sraw = sc[4096 + tl * 8 + 2 * s + (pc >> 1)];
+    dq_store<FMT, OUT>(d, gs, 16 * t + n, k0, dst, ld);
   }
 }
 
@@ -551,7 +644,19 @@ hipError_t dequant_layout(int fmt, const uint8_t* codes, const void* scales, con
                           hipStream_t stream) {
   const int64_t chunks = rows * (cols >> 3);
   if (!chunks) return hipSuccess;
-  const unsigned grid = grid_for(chunks);
+  if constexpr (LAYOUT == kLayoutTiled) {
+    const int64_t units = ((rows + 15) >> 4) * (cols >> 9);   // 16 rows x 512 k per wave
+    const unsigned tgrid = (unsigned)((units + kDqtWaves - 1) / kDqtWaves);
+#define Q4_DQT(F, O) dequant_tiled_kernel<F, O><<<tgrid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld)
+    if (dst_dtype == 0) {
+      if (fmt == 0) { Q4_DQT(0, 0); } else if (fmt == 1) { Q4_DQT(1, 0); } else if (fmt == 4) { Q4_DQT(4, 0); } else { Q4_DQT(2, 0); }
+    } else {
+      if (fmt == 0) { Q4_DQT(0, 1); } else if (fmt == 1) { Q4_DQT(1, 1); } else if (fmt == 4) { Q4_DQT(4, 1); } else { Q4_DQT(2, 1); }
+    }
+#undef Q4_DQT
+    return hipGetLastError();
+  }
+  const unsigned grid = grid_for((chunks + kDqUnroll - 1) / kDqUnroll);
   const bool idx32 = chunks <= 0xFFFFFFFFll;
 #define Q4_DQ(F, O)                                                                                              \
   if (idx32) dequant_kernel<F, O, LAYOUT, true><<<grid, kThreads, 0, stream>>>(codes, scales, gs, rows, cols, dst, ld); \
