@@ -188,6 +188,78 @@ fp8_rows_quantize_wg_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_
   }
 }
 
+// The same for rows of at most 8192 values with cols % 32 == 0, each thread
+// taking 32 consecutive values (one 32-wide group of the tiled layout): its
+// codes are two whole 16-byte operand pieces (tiled) or 32 contiguous bytes
+// (row-major), written by two 16-byte stores instead of eight 4-byte ones.
+// In the tiled layout the 16 rows of a tile share every 128-byte line of
+// its codes (8 rows each), so the rows go to workgroups of one XCD: with
+// 128 | srows, workgroup b (on XCD b % 8 in dispatch order) takes row
+// (b % 8) * srows/8 + b / 8, and each XCD's L2 sees whole lines written
+// instead of 16-byte pieces of lines shared with the other XCDs.
+template <int LAYOUT>
+__global__ void __launch_bounds__(256)
+fp8_rows_quantize_wg32_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int tid = threadIdx.x;
+  const int64_t srows = gridDim.x;
+  const int64_t r = (LAYOUT == kLayoutTiled && srows % 128 == 0)
+                        ? (int64_t)(blockIdx.x % 8) * (srows / 8) + blockIdx.x / 8
+                        : (int64_t)blockIdx.x;
+  const int64_t k0 = (int64_t)tid * 32;
+  const bool live = k0 < cols;
+  auto store32 = [&](const uint2 (&w)[4]) {
+    if constexpr (LAYOUT == kLayoutRows) {
+      uint4* d = reinterpret_cast<uint4*>(codes + r * cols + k0);
+      d[0] = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
+      d[1] = make_uint4(w[2].x, w[2].y, w[3].x, w[3].y);
+    } else {
+      // chunks 0, 1 fill the group's piece in the first operand half, 2, 3
+      // the one in the second
+      *reinterpret_cast<uint4*>(codes + fp8_tiled_dword(r, k0, cols, 0)) = make_uint4(w[0].x, w[0].y, w[1].x, w[1].y);
+      *reinterpret_cast<uint4*>(codes + fp8_tiled_dword(r, k0 + 16, cols, 0)) = make_uint4(w[2].x, w[2].y, w[3].x, w[3].y);
+    }
+  };
+  if (r >= rows) {  // padding row of the last tile: zero codes
+    if (live) {
+      const uint2 z[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
+      store32(z);
+    }
+    return;
+  }
+  const uint16_t* row = src + r * ld;
+  // every load unconditional (a thread past the row's end re-reads its first
+  // 32 values, which leave the max unchanged and are never encoded)
+  uint4 v[4];
+  const uint16_t* p = row + (live ? k0 : 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first use
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = absmax_bf16x8(v[i], amax);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float part[4];
+  if ((tid & 63) == 0) part[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+  const float s = fmaxf(amax, 1e-12f) / 448.0f;
+  if (tid == 0) scales[r] = s;
+  if (!live) return;
+  const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+  const float rcp = __builtin_amdgcn_rcpf(s);
+  const float rl = rcp * (1.0f - 0x1p-20f), rh = rcp * (1.0f + 0x1p-20f);
+  float x[8];
+  uint2 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unpack8(v[i], x);
+    w[i] = fp8_pack8<LAYOUT>(x, s, rl, rh, fast);
+  }
+  store32(w);
+}
+
 constexpr int kThreads = 256;
 
 // value = fp32(E4M3 value * row scale); 8 values per thread.
@@ -244,7 +316,12 @@ hipError_t launch_fp8_rows_quantize(int layout, const uint16_t* src, int64_t ld,
                                     int64_t cols, uint8_t* codes, float* scales, hipStream_t stream) {
   const int64_t srows = layout == kLayoutTiled ? ((rows + 15) >> 4) << 4 : rows;
   if (srows == 0 || cols == 0) return hipSuccess;
-  if (cols <= 2048 * kWgChunks) {  // a workgroup per row, the row in registers
+  if (cols <= 256 * 32 && cols % 32 == 0) {  // a workgroup per row, 32 values per thread
+    if (layout == kLayoutTiled)
+      fp8_rows_quantize_wg32_kernel<kLayoutTiled><<<(unsigned)srows, 256, 0, stream>>>(src, ld, rows, cols, codes, scales);
+    else
+      fp8_rows_quantize_wg32_kernel<kLayoutRows><<<(unsigned)srows, 256, 0, stream>>>(src, ld, rows, cols, codes, scales);
+  } else if (cols <= 2048 * kWgChunks) {  // a workgroup per row, the row in registers
     if (layout == kLayoutTiled)
       fp8_rows_quantize_wg_kernel<kLayoutTiled><<<(unsigned)srows, 256, 0, stream>>>(src, ld, rows, cols, codes, scales);
     else
