@@ -63,6 +63,39 @@ constexpr float kNudgeDown = 1.0f - 0x1p-20f, kNudgeUp = 1.0f + 0x1p-20f;
 
 __device__ __forceinline__ bool in_bracket_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
+// Value j (0..7, per lane) of eight, by a three-level select (the values
+// come in as separate scalars so the selects stay register moves).
+__device__ __forceinline__ float pick8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                       float a7, int j) {
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4;
+  const float v01 = b0 ? a1 : a0, v23 = b0 ? a3 : a2, v45 = b0 ? a5 : a4, v67 = b0 ? a7 : a6;
+  const float v03 = b1 ? v23 : v01, v47 = b1 ? v67 : v45;
+  return b2 ? v47 : v03;
+}
+
+// Codes p of a chunk whose two bracket products disagreed on the nibbles
+// set in diff: each of those values is divided by its scale (eff0 for
+// elements 0..3, eff1 for 4..7) and its code replaced, one value per pass
+// of the loop.  Exact ties (the fp32 quotient on an E2M1 midpoint) are not
+// rare: eff = fp32(E4M3 * gs) often has a short mantissa, and 2688 = 6 * 448
+// puts the factors 3 and 7 of many bf16 values into it, so several values
+// in a hundred can hit a midpoint.  Dividing only those values, rather than
+// the whole chunk whenever any lane of the wave needs one, cut the NVFP4
+// block pass on the 28672 x 8192 decode weight from 151 to ~110 us.
+__device__ __forceinline__ uint32_t e2m1_fix(const Chunk8& x, float eff0, float eff1, uint32_t p, uint32_t diff) {
+#pragma clang fp contract(off)
+  while (diff != 0u) {
+    const int j = __builtin_ctz(diff) >> 2;
+    const float v = pick8(x.v[0], x.v[1], x.v[2], x.v[3], x.v[4], x.v[5], x.v[6], x.v[7], j);
+    const float y = v / (j < 4 ? eff0 : eff1);  // fp32 division by the scale as used
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, 0.0f, 1.0f, 0) & 0xFu;
+    const uint32_t m = 0xFu << (4 * j);
+    p = (p & ~m) | (c << (4 * j));
+    diff &= ~m;
+  }
+  return p;
+}
+
 // E2M1 codes of x[j] / eff.
 __device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
 #pragma clang fp contract(off)
@@ -77,6 +110,7 @@ __device__ __forceinline__ uint32_t e2m1_pack8_div(const Chunk8& x, float eff) {
     }
     const uint32_t pl = e2m1_pack8(lo, 1.0f), ph = e2m1_pack8(hi, 1.0f);
     if (__builtin_expect(pl == ph, 1)) return pl;
+    return e2m1_fix(x, eff, eff, pl, pl ^ ph);
   }
   Chunk8 y;
 #pragma unroll
@@ -90,9 +124,11 @@ __device__ __forceinline__ uint32_t nv_scale_code(float amax, float gs, float rg
 #pragma clang fp contract(off)
   if (gs_ok) {
     const float a = amax * rgs;
-    const uint32_t cl = e4m3_encode(fminf(a * (kNudgeDown / 6.0f), 448.0f));
-    const uint32_t ch = e4m3_encode(fminf(a * (kNudgeUp / 6.0f), 448.0f));
-    if (__builtin_expect(cl == ch, 1)) return cl;
+    // both bracket values in one v_cvt_pk_fp8_f32 (E4M3, round to nearest
+    // even; the inputs are in [0, 448]): bytes 0 and 1
+    const uint32_t c2 = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(a * (kNudgeDown / 6.0f), 448.0f),
+                                                        fminf(a * (kNudgeUp / 6.0f), 448.0f), 0, false);
+    if (__builtin_expect((c2 & 0xFFu) == ((c2 >> 8) & 0xFFu), 1)) return c2 & 0xFFu;
   }
   return e4m3_encode(fminf((amax / 6.0f) / gs, 448.0f));
 }
@@ -121,13 +157,7 @@ __device__ __forceinline__ uint32_t nv_pack8_halves(const Chunk8& x, float eff0,
       hi.v[j] = x.v[j] * (r * kNudgeUp);
     }
     const uint32_t pl = e2m1_pack8(lo, 1.0f), ph = e2m1_pack8(hi, 1.0f);
-    if (__builtin_expect(pl == ph, 1)) p = pl;
-    else {
-      Chunk8 y;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) y.v[j] = x.v[j] / (j < 4 ? eff0 : eff1);
-      p = e2m1_pack8(y, 1.0f);
-    }
+    p = __builtin_expect(pl == ph, 1) ? pl : e2m1_fix(x, eff0, eff1, pl, pl ^ ph);
   } else {
     Chunk8 y;
 #pragma unroll
