@@ -59,8 +59,8 @@ __device__ __forceinline__ uint2 fp8_cvt8(const float (&f)[8]) {
 // at most 1/2 ulp, far less than the nudge); the clamp to +-448 and the
 // E4M3 rounding are monotone in the value, so where both ends give the
 // same codes, so does the quotient.  Otherwise (a quotient within about
-// 2^-20 of a rounding boundary, an exact tie), and for scales outside
-// [2^-100, 2^100], the eight values are divided.
+// 2^-20 of a rounding boundary, an exact tie) the values whose codes differ
+// are divided, and for scales outside [2^-100, 2^100] all eight are.
 template <int LAYOUT>
 __device__ __forceinline__ uint2 fp8_pack8(const float (&x)[8], float s, float rl, float rh, bool fast) {
   if (fast) {
@@ -73,6 +73,23 @@ __device__ __forceinline__ uint2 fp8_pack8(const float (&x)[8], float s, float r
     }
     const uint2 pl = fp8_cvt8(lo), ph = fp8_cvt8(hi);
     if (__builtin_expect(pl.x == ph.x && pl.y == ph.y, 1)) return pl;
+    // only the values whose codes differ are divided, one per pass (exact
+    // ties are common: s = amax / 448 has a short mantissa whenever amax's
+    // has a factor 7)
+    uint32_t w[2] = {pl.x, pl.y}, d[2] = {pl.x ^ ph.x, pl.y ^ ph.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      while (d[h] != 0u) {
+        const int b = __builtin_ctz(d[h]) >> 3;
+        const float v = pick8(x[fp8_slot<LAYOUT>(0)], x[fp8_slot<LAYOUT>(1)], x[fp8_slot<LAYOUT>(2)],
+                              x[fp8_slot<LAYOUT>(3)], x[fp8_slot<LAYOUT>(4)], x[fp8_slot<LAYOUT>(5)],
+                              x[fp8_slot<LAYOUT>(6)], x[fp8_slot<LAYOUT>(7)], 4 * h + b);
+        const uint32_t m = 0xFFu << (8 * b);
+        w[h] = (w[h] & ~m) | (fp8_code(v, s) << (8 * b));
+        d[h] &= ~m;
+      }
+    }
+    return make_uint2(w[0], w[1]);
   }
   uint32_t e[8];
 #pragma unroll

@@ -27,6 +27,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Value j (0..7, per lane) of eight, by a three-level select (the values
+// come in as separate scalars so the selects stay register moves).
+__device__ __forceinline__ float pick8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                       float a7, int j) {
+  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4;
+  const float v01 = b0 ? a1 : a0, v23 = b0 ? a3 : a2, v45 = b0 ? a5 : a4, v67 = b0 ? a7 : a6;
+  const float v03 = b1 ? v23 : v01, v47 = b1 ? v67 : v45;
+  return b2 ? v47 : v03;
+}
+
 // E2M1 code -> value (sign included).
 __device__ __forceinline__ float e2m1_value(uint32_t nib) {
   // magnitudes 0,0.5,1,1.5,2,3,4,6: exponent field e = bits 2:1, mantissa m = bit 0

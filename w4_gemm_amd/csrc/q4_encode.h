@@ -63,16 +63,6 @@ constexpr float kNudgeDown = 1.0f - 0x1p-20f, kNudgeUp = 1.0f + 0x1p-20f;
 
 __device__ __forceinline__ bool in_bracket_range(float s) { return s >= 0x1p-100f && s <= 0x1p100f; }
 
-// Value j (0..7, per lane) of eight, by a three-level select (the values
-// come in as separate scalars so the selects stay register moves).
-__device__ __forceinline__ float pick8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
-                                       float a7, int j) {
-  const bool b0 = j & 1, b1 = j & 2, b2 = j & 4;
-  const float v01 = b0 ? a1 : a0, v23 = b0 ? a3 : a2, v45 = b0 ? a5 : a4, v67 = b0 ? a7 : a6;
-  const float v03 = b1 ? v23 : v01, v47 = b1 ? v67 : v45;
-  return b2 ? v47 : v03;
-}
-
 // Codes p of a chunk whose two bracket products disagreed on the nibbles
 // set in diff: each of those values is divided by its scale (eff0 for
 // elements 0..3, eff1 for 4..7) and its code replaced, one value per pass
