@@ -125,7 +125,8 @@ def mfma_ceiling(torch, q4, dev, kind):
     below the published dense peak.  Measured once per kind, after a short
     idle gap, over about 0.2 s of back-to-back launches."""
     if kind not in _MFMA_CEILING:
-        sink = torch.zeros(q4.PROBE_MIX_SINK if kind.startswith("fp4_") else 1, dtype=torch.int32, device=dev)
+        sink = torch.zeros(q4.PROBE_MIX_SINK if kind.endswith(("_copy", "_mix")) else 1, dtype=torch.int32,
+                           device=dev)
         iters = 4096 if kind.startswith("fp4") or kind == "fp8" else 8192
         flops = [0.0]
 
@@ -371,11 +372,14 @@ def main():
         extra["mfma_ceilings_TFLOPs"] = {
             k: {"measured": round(v, 1), "published_peak": {"fp4": FP4_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS,
                                                           "fp16": FP16_PEAK_TFLOPS, "fp8": FP8_PEAK_TFLOPS,
-                                                          "fp4_copy": FP4_PEAK_TFLOPS, "fp4_mix": FP4_PEAK_TFLOPS}[k],
+                                                          "fp4_copy": FP4_PEAK_TFLOPS, "fp4_mix": FP4_PEAK_TFLOPS,
+                                                          "bf16_mix": BF16_PEAK_TFLOPS}[k],
                 "note": "random register operands, q4_mfma_probe" + (
                     "; with the tiled W4A4 kernel's global->LDS copies" + (" and LDS fragment reads"
                                                                            if k == "fp4_mix" else "")
-                    + " per 64 products per SIMD" if k.startswith("fp4_") else "")}
+                    + " per 64 products per SIMD" if k.startswith("fp4_") else "") + (
+                    "; with the tiled W4A16 kernel's NVFP4 dequantization, global->LDS copies and LDS"
+                    " fragment reads per 16 products per wave" if k == "bf16_mix" else "")}
             for k, v in _MFMA_CEILING.items()}
 
     cpu = None
@@ -436,6 +440,7 @@ def bench_nvfp4(torch, q4, workloads, dev, seed):
            "frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
            "quantize_us": round(qms * 1e3, 1),
            "quantize_GBps": round((N * K * 2 * 2 + q.nbytes) / (qms * 1e-3) / 1e9, 1)}
+    with_ceiling(res, torch, q4, dev, "bf16_mix", prefix="mix_ceiling")
     return with_ceiling(res, torch, q4, dev, "bf16")
 
 

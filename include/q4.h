@@ -364,11 +364,15 @@ q4_status q4_read_probe(const void* src, int64_t bytes, uint32_t* sink, void* st
  *                        fragment reads per 8 instructions: that kernel's
  *                        whole memory-instruction mix, so the rate its loop
  *                        can approach on this part
+ *          Q4_PROBE_BF16_MIX  the bf16 instruction with the tiled W4A16
+ *                        GEMM's mix on NVFP4 weights: per 16 instructions
+ *                        one weight fragment dequantized (their row
+ *                        operand), one copy and eight fragment reads
  *          other values: Q4_ERR_FORMAT
  *   iters  iterations of 8 instructions per wave, 0 .. 2^24 (else
  *          Q4_ERR_SHAPE); the launch runs two waves per SIMD on every
  *          compute unit; iters == 0 is a no-op (*flops = 0)
- *   sink   device uint32[1] (the two FP4 mix kinds: 16384 uint32, 16-byte
+ *   sink   device uint32[1] (the three mix kinds: 16384 uint32, 16-byte
  *          aligned, else Q4_ERR_ALIGN -- the 64 KB the copies read; their
  *          contents do not matter), written only if the folded sums equal
  *          one fixed constant (which keeps the products alive)
@@ -381,7 +385,8 @@ typedef enum q4_probe_kind {
     Q4_PROBE_F16 = 2,
     Q4_PROBE_FP8 = 3,
     Q4_PROBE_FP4_COPY = 4,
-    Q4_PROBE_FP4_MIX = 5
+    Q4_PROBE_FP4_MIX = 5,
+    Q4_PROBE_BF16_MIX = 6
 } q4_probe_kind;
 
 q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* sink, double* flops,

@@ -254,7 +254,7 @@ def test_mfma_probe_validation():
     import ctypes
     L = q4.lib()
     f = ctypes.c_double(-1.0)
-    assert L.q4_mfma_probe(6, 1, 0, A16, ctypes.byref(f), None) == FMT
+    assert L.q4_mfma_probe(7, 1, 0, A16, ctypes.byref(f), None) == FMT
     assert L.q4_mfma_probe(-1, 1, 0, A16, ctypes.byref(f), None) == FMT
     assert L.q4_mfma_probe(0, -1, 0, A16, ctypes.byref(f), None) == SHAPE
     assert L.q4_mfma_probe(0, (1 << 24) + 1, 0, A16, ctypes.byref(f), None) == SHAPE
@@ -264,7 +264,8 @@ def test_mfma_probe_validation():
     # the instruction-mix kinds copy 16 bytes per lane from the sink window
     assert L.q4_mfma_probe(4, 1, 0, A16 + 4, ctypes.byref(f), None) == ALIGN
     assert L.q4_mfma_probe(5, 1, 0, A16 + 8, ctypes.byref(f), None) == ALIGN
-    for kind in range(6):
+    assert L.q4_mfma_probe(6, 1, 0, A16 + 12, ctypes.byref(f), None) == ALIGN
+    for kind in range(7):
         f.value = -1.0
         assert L.q4_mfma_probe(kind, 0, 0, None, ctypes.byref(f), None) == OK
         assert f.value == 0.0

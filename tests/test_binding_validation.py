@@ -153,3 +153,4 @@ def test_mfma_probe_rejects():
     _raises("must be a GPU tensor", q4.q4_mfma_probe, "bf16", 16, sink)
     _raises("sink must be contiguous with at least 16384 entries", q4.q4_mfma_probe, "fp4_mix", 16, sink)
     _raises("sink must be contiguous with at least 16384 entries", q4.q4_mfma_probe, "fp4_copy", 16, sink)
+    _raises("sink must be contiguous with at least 16384 entries", q4.q4_mfma_probe, "bf16_mix", 16, sink)

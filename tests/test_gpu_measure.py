@@ -24,13 +24,13 @@ def test_read_probe_reads_and_leaves_sink():
 
 
 @pytest.mark.parametrize("kind,peak", [("fp4", 10100.0), ("bf16", 2500.0), ("fp16", 2500.0), ("fp8", 5000.0),
-                                       ("fp4_copy", 10100.0), ("fp4_mix", 10100.0)])
+                                       ("fp4_copy", 10100.0), ("fp4_mix", 10100.0), ("bf16_mix", 2500.0)])
 def test_mfma_probe_rate(kind, peak):
     """The probe reports its operation count, leaves the sink alone, and
     runs at a positive rate no higher than the published dense peak (plus
-    timing slack).  The two FP4 instruction-mix kinds read a 64 KB window
-    at the sink."""
-    n = q4.PROBE_MIX_SINK if kind.startswith("fp4_") else 1
+    timing slack).  The three instruction-mix kinds read a 64 KB window at
+    the sink."""
+    n = q4.PROBE_MIX_SINK if kind.endswith(("_copy", "_mix")) else 1
     sink = torch.full((n,), 7, dtype=torch.int32, device=DEV)
     iters = 512
     flops = q4.q4_mfma_probe(kind, iters, sink)

@@ -482,17 +482,19 @@ def q4_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     _check(lib().q4_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "q4_read_probe")
 
 
-PROBE_KINDS = {"fp4": 0, "bf16": 1, "fp16": 2, "fp8": 3, "fp4_copy": 4, "fp4_mix": 5}
-PROBE_MIX_SINK = 16384   # int32 entries the "fp4_copy" / "fp4_mix" kinds read (64 KB)
+PROBE_KINDS = {"fp4": 0, "bf16": 1, "fp16": 2, "fp8": 3, "fp4_copy": 4, "fp4_mix": 5, "bf16_mix": 6}
+PROBE_MIX_SINK = 16384   # int32 entries the "fp4_copy" / "fp4_mix" / "bf16_mix" kinds read (64 KB)
 
 
 def q4_mfma_probe(kind: str, iters: int, sink: torch.Tensor, seed: int = 1, stream=None) -> float:
     """Measurement helper: back-to-back matrix instructions of one kind
     ("fp4", "bf16", "fp16", "fp8") on random register operands, or the FP4
     instruction with the tiled W4A4 kernel's global->LDS copies
-    ("fp4_copy") or its copies and LDS fragment reads ("fp4_mix") mixed in;
-    returns the launch's floating-point operations.  sink: int32 GPU tensor
-    [1] ([PROBE_MIX_SINK], 16-byte aligned, for the two mix kinds)."""
+    ("fp4_copy") or its copies and LDS fragment reads ("fp4_mix") mixed in,
+    or the bf16 instruction with the tiled W4A16 GEMM's NVFP4 dequantization,
+    copies and fragment reads ("bf16_mix"); returns the launch's
+    floating-point operations.  sink: int32 GPU tensor [1] ([PROBE_MIX_SINK],
+    16-byte aligned, for the three mix kinds)."""
     if kind not in PROBE_KINDS:
         raise ValueError(f"kind must be one of {sorted(PROBE_KINDS)}")
     if not isinstance(iters, int) or iters < 0 or iters > (1 << 24):

@@ -364,7 +364,7 @@ q4_status q4_moe_combine(const void* y_bf16, int64_t ldy, const int32_t* inv, co
 
 q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* sink, double* flops,
                         void* stream) {
-  if (kind < Q4_PROBE_FP4 || kind > Q4_PROBE_FP4_MIX) return Q4_ERR_FORMAT;
+  if (kind < Q4_PROBE_FP4 || kind > Q4_PROBE_BF16_MIX) return Q4_ERR_FORMAT;
   if (iters < 0 || iters > ((int64_t)1 << 24)) return Q4_ERR_SHAPE;
   if (!flops) return Q4_ERR_NULL;
   *flops = 0.0;
@@ -374,7 +374,8 @@ q4_status q4_mfma_probe(int32_t kind, int64_t iters, uint32_t seed, uint32_t* si
   if (!aligned(sink, kind >= Q4_PROBE_FP4_COPY ? 16 : 4)) return Q4_ERR_ALIGN;
   const int grid = q4::mfma_probe_grid();
   if (grid <= 0) return hip_status(hipErrorInvalidDevice);
-  const double per = (kind == Q4_PROBE_BF16 || kind == Q4_PROBE_F16) ? 2.0 * 16 * 16 * 32 : 2.0 * 16 * 16 * 128;
+  const double per = (kind == Q4_PROBE_BF16 || kind == Q4_PROBE_F16 || kind == Q4_PROBE_BF16_MIX)
+                         ? 2.0 * 16 * 16 * 32 : 2.0 * 16 * 16 * 128;
   const q4_status st = hip_status(q4::launch_mfma_probe(kind, iters, seed, sink, grid, as_stream(stream)));
   if (st == Q4_OK) *flops = (double)grid * 4 * 8 * (double)iters * per;
   return st;

@@ -33,7 +33,10 @@
 // pointer (L2-resident), each wave into its own ring of four 1 KB LDS
 // slots; the reads take a wave's own 4 KB of LDS.  The difference to kind
 // 0 is what those instructions cost the matrix core (issue slots, and the
-// clock, which power sets).
+// clock, which power sets).  Kind 6 does the same for the tiled W4A16 GEMM
+// on NVFP4 weights: bf16 products with, per wave and 16 of them, one
+// weight fragment dequantized by that kernel's own helper (the row operand
+// of those 16 products), 8 fragment reads and one copy.
 #include "q4_launch.h"
 #include "q4_mma.h"
 
@@ -80,11 +83,13 @@ __device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
 }
 
 // KIND: 0 FP4 16x16x128 (scaled), 1 bf16 16x16x32, 2 fp16 16x16x32, 3 FP8 16x16x128 (scaled),
-// 4 FP4 with one copy per 8 instructions, 5 FP4 with one copy and three fragment reads per 8
+// 4 FP4 with one copy per 8 instructions, 5 FP4 with one copy and three fragment reads per 8,
+// 6 bf16 with one dequantized NVFP4 fragment, one copy and eight fragment reads per 16
 template <int KIND>
 __global__ void __launch_bounds__(kMfmaProbeWaves * 64)
 mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
-  constexpr bool kCopy = KIND >= 4, kRead = KIND == 5;
+  constexpr bool kCopy = KIND >= 4, kRead = KIND >= 5, kDq = KIND == 6;
+  constexpr int kReads = KIND == 6 ? 4 : 3;  // fragment reads per 8 instructions
   // per wave: four 1 KB copy slots, then 4 KB of fragments to read
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kCopy ? kMfmaProbeWaves * 8192 : 16];
   const uint32_t base = (seed * 0x9E3779B1u) ^ ((blockIdx.x * blockDim.x + threadIdx.x) * 64u);
@@ -95,7 +100,7 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t a = probe_hash(base + 8u * i + e), b = probe_hash(base + 8u * i + 4u + e + 0x51ED27u);
-      if constexpr (KIND == 1) {  // bf16: random signs and mantissas, exponents of [0.5, 1)
+      if constexpr (KIND == 1 || KIND == 6) {  // bf16: random signs and mantissas, exponents of [0.5, 1)
         a = (a & 0x807F807Fu) | 0x3F003F00u;
         b = (b & 0x807F807Fu) | 0x3F003F00u;
       } else if constexpr (KIND == 2) {  // fp16: the same
@@ -126,7 +131,11 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
   uint8_t* const ring = lds + (kCopy ? wave * 8192 : 0);
   const uint8_t* const csrc = reinterpret_cast<const uint8_t*>(sink) + lane * 16;
   const int cbase = blockIdx.x * kMfmaProbeWaves + wave;
-  u32x4_t r[2][3] = {};
+  u32x4_t r[2][4] = {};
+  // kind 6: the NVFP4 codes dequantized per 16 products, and their result
+  const uint32_t dcodes = probe_hash(base + 4242u);
+  const float dscale = e4m3_value(0x3Fu ^ (probe_hash(base + 99u) & 0x07u)) * 0x1p-9f;
+  u32x4_t wq = y[0];
   if constexpr (kRead) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) reinterpret_cast<uint32_t*>(ring + 4096)[lane + 64 * j] = probe_hash(base + 977u * j);
@@ -135,13 +144,22 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
   const uint32_t fra = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(ring + 4096) + lane * 16;
   auto iteration = [&](int64_t it, auto set) {
     constexpr int R = decltype(set)::value;  // register set of this iteration's fragment reads
+    if constexpr (kDq) {
+      if constexpr (R == 0) {  // this pair of iterations' row operand
+        wq = __builtin_bit_cast(u32x4_t, dq8_e2m1_mul(dcodes ^ (uint32_t)it, dscale));
+        asm volatile("" : "+v"(wq));
+      }
+    }
     asm volatile("s_nop 4");  // the operands' last vector writes before the first product
-    if constexpr (kRead)
+    if constexpr (kRead && kReads == 3)
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[R ^ 1][0]), "+v"(r[R ^ 1][1]), "+v"(r[R ^ 1][2]) :: "memory");
+    if constexpr (kRead && kReads == 4)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(r[R ^ 1][0]), "+v"(r[R ^ 1][1]), "+v"(r[R ^ 1][2]), "+v"(r[R ^ 1][3]) :: "memory");
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if constexpr (kCopy) {
-        if (i == 1)
+        if (i == 1 && (!kDq || R == 0))
           __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(csrc + ((cbase + it) & 63) * 1024),
                                            (__attribute__((address_space(3))) void*)(ring + (it & 3) * 1024), 16, 0, 0);
       }
@@ -149,16 +167,18 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
         // three 16-byte reads early in each iteration into register set R;
         // the next iteration starts by waiting for them (long landed) and
         // taking them as read, so their registers stay theirs until then
-        if (i < 3) {
+        if (i < kReads) {
           const uint32_t addr = fra + (uint32_t)(((it + i) & 3) * 1024);
           asm volatile("ds_read_b128 %0, %1" : "=v"(r[R][i]) : "v"(addr) : "memory");
         }
       }
-      if constexpr (KIND == 0 || KIND >= 4)
+      if constexpr (KIND == 0 || KIND == 4 || KIND == 5)
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
                      : "+v"(c[i]) : "v"(x[i]), "v"(y[i]), "v"(sc));
       else if constexpr (KIND == 1)
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[i]) : "v"(x[i]), "v"(y[i]));
+      else if constexpr (KIND == 6)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c[i]) : "v"(wq), "v"(x[i]));
       else if constexpr (KIND == 2)
         asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c[i]) : "v"(x[i]), "v"(y[i]));
       else
@@ -184,8 +204,9 @@ mfma_probe_kernel(int64_t iters, uint32_t seed, uint32_t* __restrict__ sink) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) w ^= r[s][j][0] ^ r[s][j][1] ^ r[s][j][2] ^ r[s][j][3];
+      for (int j = 0; j < kReads; ++j) w ^= r[s][j][0] ^ r[s][j][1] ^ r[s][j][2] ^ r[s][j][3];
   }
+  if constexpr (kDq) w ^= wq[0] ^ wq[3];
   if constexpr (kCopy) w ^= reinterpret_cast<const uint32_t*>(ring)[lane];
   if (w == kProbeMagic) sink[0] = w;
 }
@@ -207,7 +228,8 @@ hipError_t launch_mfma_probe(int kind, int64_t iters, uint32_t seed, uint32_t* s
     case 2: mfma_probe_kernel<2><<<g, b, 0, stream>>>(iters, seed, sink); break;
     case 3: mfma_probe_kernel<3><<<g, b, 0, stream>>>(iters, seed, sink); break;
     case 4: mfma_probe_kernel<4><<<g, b, 0, stream>>>(iters, seed, sink); break;
-    default: mfma_probe_kernel<5><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    case 5: mfma_probe_kernel<5><<<g, b, 0, stream>>>(iters, seed, sink); break;
+    default: mfma_probe_kernel<6><<<g, b, 0, stream>>>(iters, seed, sink); break;
   }
   return hipGetLastError();
 }
