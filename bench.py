@@ -335,6 +335,16 @@ def main():
             "frac_hbm": round(fbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": fbytes,
             "weight_reads": reads}
         del ef
+    # a row-major quantization of the same weight moved to the tiled layout
+    # (q4_relayout: codes and scales read once and written once)
+    rq = q4.quantize(W, "mxfp4", layout="rows")
+    rt = q4.empty_q4("mxfp4", N, K, device=dev, layout="tiled")
+    rms = timed(torch, lambda: q4.q4_relayout(rq, rt), 10, 3)
+    rbytes = rq.nbytes + rt.nbytes
+    extra["relayout_mxfp4_28672x8192_rows_to_tiled"] = {
+        "us": round(rms * 1e3, 2), "GBps": round(rbytes / (rms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "bytes": rbytes}
+    del rq, rt
     dq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
     dms = timed(torch, lambda: q4.q4_dequant(copies[0], dq), 10, 3)
     dbytes = wbytes + N * K * 2

@@ -160,6 +160,23 @@ q4_status q4_sizes(int fmt, int layout, int64_t rows, int64_t cols, size_t* code
                    size_t* scales_bytes);
 
 /*
+ * Moves a quantized tensor from one layout to the other (row-major <->
+ * tiled, the layouts above), bit for bit: the same codes and scales at the
+ * other layout's positions, the NVFP4 global scale copied.  Tiled padding
+ * rows receive the quantization of zeros (as q4_quantize writes them).  The
+ * GEMM kernels are built for the tiled layout (its fragments are contiguous
+ * kilobytes; "Low-bit inference for very large MoE", "A few details":
+ * pre-shuffled weights), so weights quantized or packed row-major are worth
+ * converting once, when they are loaded.
+ *   src, dst  the same fmt (not Q4_FP8_ROW: Q4_ERR_FORMAT), rows and cols
+ *             (else Q4_ERR_SHAPE); each validated like any q4_tensor (the
+ *             tiled one needs cols % 512 == 0).  Equal layouts: a copy.
+ *   dst must not overlap src.  Empty tensors: only the NVFP4 global scale
+ *   is copied.
+ */
+q4_status q4_relayout(const q4_tensor* src, const q4_tensor* dst, void* stream);
+
+/*
  * Quantize a bf16 matrix src [dst->rows][ld] (first dst->cols columns) into
  * dst, by round-to-nearest absmax block quantization along each row
  * ("LLM quantization", the absmax method: the group's largest magnitude

@@ -248,6 +248,26 @@ def test_gemm_quantized_validation():
     assert R(0, A16, 512, None, by(w), by(desc(rows=0, cols=512)), None) == OK
 
 
+def test_relayout_validation():
+    """q4_relayout checks both descriptors and their agreement before any
+    HIP call; an empty non-NVFP4 tensor is a no-op."""
+    L = q4.lib()
+    by = ctypes.byref
+    T = 1
+    src, dst = desc(cols=512), desc(cols=512, layout=T)
+    assert L.q4_relayout(None, by(dst), None) == NULL
+    assert L.q4_relayout(by(src), None, None) == NULL
+    assert L.q4_relayout(by(src), by(desc(fmt=q4.INT4_G128, cols=512, layout=T)), None) == FMT
+    assert L.q4_relayout(by(desc(fmt=q4.FP8_ROW, cols=512)), by(desc(fmt=q4.FP8_ROW, cols=512, layout=T)),
+                         None) == FMT
+    assert L.q4_relayout(by(src), by(desc(rows=48, cols=512, layout=T)), None) == SHAPE
+    assert L.q4_relayout(by(desc(cols=256)), by(desc(cols=256, layout=T)), None) == SHAPE   # tiled: cols % 512
+    assert L.q4_relayout(by(src), by(desc(cols=512, codes=A16 + 4, layout=T)), None) == ALIGN
+    assert L.q4_relayout(by(desc(fmt=q4.NVFP4, cols=512)), by(desc(fmt=q4.NVFP4, cols=512, gs=A16, layout=T)),
+                         None) == NULL                                      # src without its global scale
+    assert L.q4_relayout(by(desc(rows=0, cols=512)), by(desc(rows=0, cols=512, layout=T)), None) == OK
+
+
 def test_mfma_probe_validation():
     """Argument checks of the matrix-instruction probe; iters == 0 returns
     before any device query, so this runs without a GPU."""

@@ -144,6 +144,15 @@ def test_moe_helpers_reject():
     _raises("must be a GPU tensor", q4.q4_moe_combine, y, r, torch.zeros(T, N, dtype=BF16))
 
 
+def test_relayout_rejects():
+    a = q4.empty_q4("mxfp4", 32, 512, device="cpu")
+    b = q4.empty_q4("mxfp4", 32, 512, device="cpu", layout="tiled")
+    _raises("same format and shape", q4.q4_relayout, a, q4.empty_q4("nvfp4", 32, 512, device="cpu", layout="tiled"))
+    _raises("same format and shape", q4.q4_relayout, a, q4.empty_q4("mxfp4", 48, 512, device="cpu", layout="tiled"))
+    _raises("must be a Q4Tensor", q4.q4_relayout, a, b.codes)
+    _raises("must be a GPU tensor", q4.q4_relayout, a, b)
+
+
 def test_mfma_probe_rejects():
     sink = torch.zeros(1, dtype=I32)
     _raises("kind must be one of", q4.q4_mfma_probe, "int8", 16, sink)

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "INT4_G128", "MXFP4", "NVFP4", "FP8_ROW", "INT4_ZP", "FORMAT_NAMES", "GROUP", "Q4Error", "Q4Tensor",
     "LAYOUT_ROWS", "LAYOUT_TILED", "LAYOUT_NAMES",
-    "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
+    "lib", "q4_version", "q4_sizes", "q4_quantize", "q4_dequant", "q4_relayout", "relayout", "q4_gemv", "q4_gemm", "q4_gemm_quantized",
     "q4_grouped_gemm", "q4_grouped_gemm_swiglu", "q4_moe_route", "q4_swiglu", "q4_moe_combine",
     "moe_layer", "interleave_gate_up", "q4_read_probe", "q4_mfma_probe", "PROBE_KINDS", "PROBE_MIX_SINK",
     "empty_q4", "quantize", "LIB_PATH",
@@ -78,6 +78,7 @@ def _lib_handle():
                           ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "q4_quantize": ([vp, i64, P, vp, vp], ctypes.c_int),
             "q4_dequant": ([P, vp, ctypes.c_int, i64, vp], ctypes.c_int),
+            "q4_relayout": ([P, P, vp], ctypes.c_int),
             "q4_gemv": ([P, vp, i64, i64, vp, i64, vp], ctypes.c_int),
             "q4_gemm": ([i64, vp, i64, P, P, vp, i64, vp], ctypes.c_int),
             "q4_gemm_quantized": ([i64, vp, i64, P, P, P, vp, vp], ctypes.c_int),
@@ -274,6 +275,26 @@ def quantize(src: torch.Tensor, fmt, nv_global_in: Optional[torch.Tensor] = None
     """Allocate a Q4Tensor on src's device and quantize src into it."""
     dst = empty_q4(fmt, src.shape[0], src.shape[1], device=src.device, layout=layout)
     return q4_quantize(src, dst, nv_global_in, stream)
+
+
+def q4_relayout(src: Q4Tensor, dst: Q4Tensor, stream=None) -> Q4Tensor:
+    """Copy src into dst's layout (row-major <-> tiled), bit for bit; same
+    format and shape.  The GEMM kernels want the tiled layout."""
+    _q4(src, "src")
+    _q4(dst, "dst")
+    if src.fmt != dst.fmt or (src.rows, src.cols) != (dst.rows, dst.cols):
+        raise ValueError("src and dst must have the same format and shape")
+    _on_gpu(("src", src), ("dst", dst))
+    a, b = src.c(), dst.c()
+    _check(lib().q4_relayout(ctypes.byref(a), ctypes.byref(b), _stream(stream)), "q4_relayout")
+    return dst
+
+
+def relayout(src: Q4Tensor, layout=LAYOUT_TILED, stream=None) -> Q4Tensor:
+    """Allocate a tensor of src's format and shape in `layout` and move src
+    into it."""
+    dst = empty_q4(src.fmt, src.rows, src.cols, device=src.codes.device, layout=layout)
+    return q4_relayout(src, dst, stream)
 
 
 def q4_dequant(src: Q4Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:

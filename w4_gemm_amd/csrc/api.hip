@@ -152,6 +152,32 @@ q4_status q4_dequant(const q4_tensor* src, void* dst, int dst_dtype, int64_t ld,
                                        dst_dtype, ld, as_stream(stream)));
 }
 
+q4_status q4_relayout(const q4_tensor* src, const q4_tensor* dst, void* stream) {
+  q4_status st = check_tensor(src);
+  if (st != Q4_OK) return st;
+  st = check_tensor(dst);
+  if (st != Q4_OK) return st;
+  if (src->fmt != dst->fmt || src->fmt == Q4_FP8_ROW) return Q4_ERR_FORMAT;
+  if (src->rows != dst->rows || src->cols != dst->cols) return Q4_ERR_SHAPE;
+  hipStream_t s = as_stream(stream);
+  if (src->fmt == Q4_NVFP4 && (src->rows == 0 || src->cols == 0 || src->layout == dst->layout)) {
+    const hipError_t e = hipMemcpyAsync(dst->global_scale, src->global_scale, 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (src->rows == 0 || src->cols == 0) return Q4_OK;
+  if (src->layout == dst->layout) {  // same layout: a copy
+    size_t cb = 0, sb = 0;
+    st = q4_sizes(src->fmt, src->layout, src->rows, src->cols, &cb, &sb);
+    if (st != Q4_OK) return st;
+    hipError_t e = hipMemcpyAsync(dst->codes, src->codes, cb, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(dst->scales, src->scales, sb, hipMemcpyDeviceToDevice, s);
+    return hip_status(e);
+  }
+  return hip_status(q4::launch_relayout(src->fmt, dst->layout, static_cast<const uint8_t*>(src->codes), src->scales,
+                                        src->global_scale, static_cast<uint8_t*>(dst->codes), dst->scales,
+                                        dst->global_scale, src->rows, src->cols, s));
+}
+
 q4_status q4_gemv(const q4_tensor* W, const void* x_bf16, int64_t B, int64_t ldx, void* y_bf16,
                   int64_t ldy, void* stream) {
   q4_status st = check_tensor(W);

@@ -58,6 +58,9 @@ hipError_t launch_quantize(int fmt, int layout, const uint16_t* src, int64_t ld,
                            const float* gs_in, hipStream_t stream);
 
 // Dequantize into row-major dst [rows][ld], dst_dtype 0 bf16 / 1 fp32.
+hipError_t launch_relayout(int fmt, int to_layout, const uint8_t* src_codes, const void* src_scales,
+                           const float* src_gs, uint8_t* dst_codes, void* dst_scales, float* dst_gs, int64_t rows,
+                           int64_t cols, hipStream_t stream);
 hipError_t launch_dequant(int fmt, int layout, const uint8_t* codes, const void* scales,
                           const float* gs, int64_t rows, int64_t cols, void* dst, int dst_dtype,
                           int64_t ld, hipStream_t stream);
