@@ -37,6 +37,11 @@
 namespace q4 {
 namespace {
 
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(nt_u32x4{a, b, c, d}, reinterpret_cast<nt_u32x4*>(p));
+}
+
 constexpr int kThreads = 256;
 
 // INT4 codes, clamp(rne(w / s), -8, 7) or, with a zero point z in [-8, 7],
@@ -316,7 +321,7 @@ quantize_block_kernel(const uint16_t* __restrict__ src, int64_t ld, int64_t rows
   if (store) {
     uint8_t* dst = LAYOUT == kLayoutTiled ? codes + ((band * S + s) << 10) + lane * 16
                                           : codes + r * (cols >> 1) + 64 * s + 16 * g;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    store16_nt(dst, packed[0], packed[1], packed[2], packed[3]);
   }
 }
 
@@ -393,6 +398,10 @@ __global__ void set_word_kernel(uint32_t* p, uint32_t v) { *p = v; }
 // Split in two so that a lane can issue the loads of several chunks before
 // it converts the first: dq_load fetches the 8 codes and the raw scale
 // field, dq_store converts and writes them.
+// Outputs are written with non-temporal stores: dequantized values (470 MB
+// of bf16 for the 28672 x 8192 weight: 107 -> 91 us in both layouts) and
+// the quantizer's codes (MXFP4 tiled 106 -> 104 us, NVFP4 192 -> 183) are
+// not read back by the kernel and would only evict other lines from L2.
 struct DqIn {
   uint32_t packed;  // 8 codes, element j in nibble j
   uint32_t sraw;    // the scale field as stored (fp16 bits, E8M0, E4M3, or the INT4-zp word)
@@ -440,15 +449,15 @@ __device__ __forceinline__ void dq_store(DqIn d, float gs, int64_t r, int64_t k0
         o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 1));
         o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 2));
         o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, s, 3));
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
+        store16_nt(reinterpret_cast<uint16_t*>(dst) + r * ld + k0, o.x, o.y, o.z, o.w);
       } else {
         const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 0);
         const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 1);
         const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 2);
         const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, s, 3);
-        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
-        o[0] = make_float4(p0[0], p0[1], p1[0], p1[1]);
-        o[1] = make_float4(p2[0], p2[1], p3[0], p3[1]);
+        float* o = reinterpret_cast<float*>(dst) + r * ld + k0;
+        store16_nt(o, f2u(p0[0]), f2u(p0[1]), f2u(p1[0]), f2u(p1[1]));
+        store16_nt(o + 4, f2u(p2[0]), f2u(p2[1]), f2u(p3[0]), f2u(p3[1]));
       }
       return;
     }
@@ -469,11 +478,11 @@ __device__ __forceinline__ void dq_store(DqIn d, float gs, int64_t r, int64_t k0
     o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
     o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
     o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + r * ld + k0) = o;
+    store16_nt(reinterpret_cast<uint16_t*>(dst) + r * ld + k0, o.x, o.y, o.z, o.w);
   } else {
-    float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(dst) + r * ld + k0);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    float* o = reinterpret_cast<float*>(dst) + r * ld + k0;
+    store16_nt(o, f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3]));
+    store16_nt(o + 4, f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7]));
   }
 }
 
