@@ -148,6 +148,32 @@ def test_gemv_deterministic(layout):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemv_row_major_scales_at_any_alignment(fmt):
+    """The row-major GEMV loads a step's row scales in vector loads when K %
+    512 == 0 and the scale rows are aligned to the vector, and one scale per
+    super-chunk otherwise: the same tensor with its scales 4 bytes off that
+    alignment gives the same bytes."""
+    N, K = 300, 2048
+    w = workloads.matrix("tg/salign", N, K, 0.02, seed=31)
+    qg, _ = quantized(w, fmt, "rows")
+    x = workloads.matrix("tg/salignx", 16, K, 1.0, seed=32).to(DEV)
+    nb = qg.scales.numel() * qg.scales.element_size()
+    buf = torch.empty(nb + 64, dtype=torch.uint8, device=DEV)
+    base = (-buf.data_ptr()) % 16                       # 16-byte aligned start inside buf
+    off = buf[base + 4: base + 4 + nb]                  # 4-byte aligned, not 8- or 16-byte
+    off.copy_(qg.scales.reshape(-1).view(torch.uint8))
+    qo = q4.Q4Tensor(qg.fmt, N, K, qg.codes, off.view(qg.scales.dtype).reshape(qg.scales.shape),
+                     qg.global_scale, qg.layout)
+    assert qo.scales.data_ptr() % 16 == 4
+    a = torch.empty((16, N), dtype=torch.bfloat16, device=DEV)
+    b = torch.empty_like(a)
+    q4.q4_gemv(qg, x, a)
+    q4.q4_gemv(qo, x, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_full_int4_gemv(layout):
     wl = workloads.int4_gemv()
