@@ -145,3 +145,44 @@ def test_graph_relayout():
         return _q4_outs(dst)
 
     _check_replays(fn, _scribble, lambda: q4.q4_quantize(w, src))
+
+
+def test_graph_w4a8_w4a4nv_dequant():
+    """The other GEMM chains (activation quantize, then the GEMM) and the
+    dequantizer: W4A8 (per-token FP8 activations x INT4 weights), W4A4 NVFP4
+    (the activation's tensor amax recomputed inside the graph), and MXFP4 /
+    NVFP4 weights dequantized to bf16 and fp32."""
+    log("graph w4a8, w4a4 nvfp4, dequant")
+    M, N, K = 96, 272, 1024
+    A = _rand((M, K), 12)
+    A2 = _rand((M, K), 13, 4.0)
+    W = _rand((N, K), 14, 0.02)
+    qw8 = q4.quantize(W, "int4", layout="tiled")
+    qwn = q4.quantize(W, "nvfp4", layout="tiled")
+    qwm = q4.quantize(W, "mxfp4", layout="tiled")
+    qwr = q4.quantize(W, "nvfp4", layout="rows")
+    qa8 = q4.empty_q4("fp8_row", M, K, device=DEV, layout="tiled")
+    qan = q4.empty_q4("nvfp4", M, K, device=DEV, layout="tiled")
+    C8 = torch.empty(M, N, device=DEV, dtype=torch.bfloat16)
+    Cn = torch.empty_like(C8)
+    D16 = torch.empty(N, K, device=DEV, dtype=torch.bfloat16)
+    D32 = torch.empty(N, K, device=DEV, dtype=torch.float32)
+    other_a8 = q4.empty_q4("fp8_row", M, K, device=DEV, layout="tiled")
+    other_an = q4.empty_q4("nvfp4", M, K, device=DEV, layout="tiled")
+
+    def fn():
+        q4.q4_quantize(A, qa8)
+        q4.q4_gemm(qa8, qw8, C8)
+        q4.q4_quantize(A, qan)
+        q4.q4_gemm(qan, qwn, Cn)
+        q4.q4_dequant(qwm, D16)
+        q4.q4_dequant(qwr, D32)
+        return [C8, Cn, D16, D32] + _q4_outs(qa8) + _q4_outs(qan)
+
+    def other():
+        # a larger-amax tensor through the same quantizers and GEMMs
+        q4.q4_quantize(A2, other_a8)
+        q4.q4_quantize(A2, other_an)
+        q4.q4_gemm(other_an, qwn, Cn)
+
+    _check_replays(fn, _scribble, other)
