@@ -97,3 +97,34 @@ def test_gemm_on_relayout_weights_is_the_tiled_gemm():
     q4.q4_gemm(qa, wm, C2)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
+
+
+def _offset_scales(q: q4.Q4Tensor, copy: bool) -> q4.Q4Tensor:
+    """The same tensor with its scales 4 bytes off 16-byte alignment."""
+    nb = q.scales.numel() * q.scales.element_size()
+    buf = torch.empty(nb + 64, dtype=torch.uint8, device=DEV)
+    base = (-buf.data_ptr()) % 16
+    off = buf[base + 4: base + 4 + nb]
+    if copy:
+        off.copy_(q.scales.reshape(-1).view(torch.uint8))
+    out = q4.Q4Tensor(q.fmt, q.rows, q.cols, q.codes, off.view(q.scales.dtype).reshape(q.scales.shape),
+                      q.global_scale, q.layout)
+    assert out.scales.data_ptr() % 16 == 4
+    return out
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_relayout_scales_at_any_alignment(fmt):
+    """Scales aligned to 16 bytes move in whole row groups, others byte by byte;
+    both give the other layout's quantization exactly, in both directions."""
+    rows, cols = 37, 1024
+    log("relayout unaligned scales", fmt)
+    wd = _weight(rows, cols, 99).to(DEV)
+    qr = q4.quantize(wd, fmt, layout="rows")
+    qt = q4.quantize(wd, fmt, layout="tiled")
+    moved = q4.relayout(_offset_scales(qr, True), "tiled")       # unaligned source
+    dst = _offset_scales(q4.empty_q4(fmt, rows, cols, device=DEV, layout="rows"), False)
+    q4.q4_relayout(qt, dst)                                       # unaligned destination
+    torch.cuda.synchronize()
+    _same(moved, qt)
+    _same(dst, qr)
