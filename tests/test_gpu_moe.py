@@ -201,3 +201,41 @@ def test_moe_layer_fused(fmt):
     ref, rr = oracle.moe_layer(to_f32(x), lg, k, oracle.quantize(fmt, to_f32(wgu)),
                                oracle.quantize(fmt, to_f32(wd)), I)
     _check_layer(out, ref, f"moe layer fused {fmt}")
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (16, 4), (70, 3)])
+def test_route_nan_logits_fill_every_slot(E, k):
+    """NaN router logits have no order in the pages, but the routing stays a
+    routing: every one of the token's k slots names a distinct expert (the
+    outputs start filled with -1, through the C ABI), the dispatch order is a
+    permutation, and tokens without NaN route exactly as the oracle does."""
+    log("route nan", E, k)
+    T = 12
+    lg = _logits(T, E, seed=83)
+    lg[0, 3] = np.nan
+    lg[1, :] = np.nan                                   # all NaN
+    lg[2, 5] = -np.float32(np.nan)                       # sign bit set
+    lg[4, : min(E, 6)] = np.nan
+    d = torch.from_numpy(lg).to(DEV)
+    ids = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), -1.0, dtype=torch.float32, device=DEV)
+    off = torch.full((E + 1,), -1, dtype=torch.int32, device=DEV)
+    gather = torch.full((T * k,), -1, dtype=torch.int32, device=DEV)
+    inv = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+    rc = q4.lib().q4_moe_route(q4._ptr(d), E, T, E, k, q4._ptr(ids), q4._ptr(w), q4._ptr(off), q4._ptr(gather),
+                               q4._ptr(inv), None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    ids_h, off_h, g_h, inv_h = ids.cpu().numpy(), off.cpu().numpy(), gather.cpu().numpy(), inv.cpu().numpy()
+    for t in range(T):
+        assert len(set(ids_h[t])) == k and ids_h[t].min() >= 0 and ids_h[t].max() < E, (t, ids_h[t])
+    assert off_h[0] == 0 and off_h[E] == T * k and (np.diff(off_h) >= 0).all()
+    assert sorted(inv_h.reshape(-1)) == list(range(T * k))
+    for i, pos in enumerate(inv_h.reshape(-1)):
+        assert g_h[pos] == i // k
+        e = ids_h.reshape(-1)[i]
+        assert off_h[e] <= pos < off_h[e + 1]
+    clean = [t for t in range(T) if not np.isnan(lg[t]).any()]
+    ref = oracle.moe_route(np.ascontiguousarray(lg[clean]), k)
+    assert np.array_equal(ids_h[clean], ref.ids)
+    assert np.allclose(w.cpu().numpy()[clean].astype(np.float64), ref.weights, rtol=2e-6, atol=1e-30)

@@ -20,8 +20,21 @@ namespace {
 constexpr int kMaxLogitsPerLane = 16;  // E <= 1024 = 16 per lane of one wave
 constexpr int kRouteWaves = 4;
 
+// Logits are ordered by integer keys that order floats as their values do
+// (-0 folded into +0; NaN above +inf when its sign is clear, below -inf
+// otherwise), so that NaN logits still leave a strict order in which every
+// chosen expert is a distinct valid one.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // One wave per token: softmax statistics over the E logits, then k rounds
-// of a wave-wide argmax (largest value, ties to the lower expert id).
+// of a wave-wide argmax (largest key, ties to the lower expert id).
 __global__ void __launch_bounds__(64 * kRouteWaves)
 moe_topk_kernel(const float* __restrict__ logits, int64_t ld, int T, int E, int k,
                 int32_t* __restrict__ ids, float* __restrict__ weights) {
@@ -47,31 +60,74 @@ moe_topk_kernel(const float* __restrict__ logits, int64_t ld, int T, int E, int 
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
   uint32_t used = 0;
   for (int j = 0; j < k; ++j) {
-    // the lane's best remaining logit (lowest expert id on ties)
-    float bv = -INFINITY;
+    // the lane's best remaining logit (lowest expert id on ties; a lane with
+    // none left keeps key 0 and id INT_MAX, below every valid candidate)
+    uint32_t bk = 0u;
     int be = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kMaxLogitsPerLane; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && !((used >> i) & 1u) && (v[i] > bv || be == 0x7FFFFFFF)) {
-        bv = v[i];
+      const uint32_t ki = order_key(v[i]);
+      if (e < E && !((used >> i) & 1u) && (ki > bk || (ki == bk && e < be))) {
+        bk = ki;
         be = e;
       }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
+      const uint32_t ok = __shfl_xor(bk, off);
       const int oe = __shfl_xor(be, off);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
+      if (ok > bk || (ok == bk && oe < be)) {
+        bk = ok;
         be = oe;
       }
     }
     if ((be & 63) == lane) used |= 1u << (be >> 6);
     if (lane == 0) {
       ids[(int64_t)t * k + j] = be;
-      weights[(int64_t)t * k + j] = expf(bv - m) / s;
+      weights[(int64_t)t * k + j] = expf(key_value(bk) - m) / s;
     }
+  }
+}
+
+// E <= 64: one logit per lane, and each chosen expert's slot is its rank
+// among the token's logits in the same order (larger key first, the lower
+// expert id on ties), counted against the keys copied to LDS -- one pass
+// instead of k rounds of a wave-wide argmax.  The ranks are a permutation,
+// so each of the k slots is written exactly once.  The softmax statistics
+// are reduced as above (same order, same bits).
+__global__ void __launch_bounds__(64 * kRouteWaves)
+moe_topk64_kernel(const float* __restrict__ logits, int64_t ld, int T, int E, int k,
+                  int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kRouteWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * kRouteWaves + w;
+  if (t >= T) return;                      // (whole waves: no barrier below)
+  const bool valid = lane < E;
+  const float v = valid ? logits[(int64_t)t * ld + lane] : -INFINITY;
+  float m = fmaxf(-INFINITY, v);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float s = valid ? expf(v - m) : 0.0f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  // lanes past E hold the smallest key; their ids are above every valid one,
+  // so they never rank ahead of a valid lane
+  const uint32_t key = valid ? order_key(v) : 0u;
+  keys[w][lane] = key;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; j += 4) {
+    const uint4 q = *reinterpret_cast<const uint4*>(&keys[w][j]);
+    rank += (q.x > key || (q.x == key && j < lane)) + (q.y > key || (q.y == key && j + 1 < lane)) +
+            (q.z > key || (q.z == key && j + 2 < lane)) + (q.w > key || (q.w == key && j + 3 < lane));
+  }
+  if (valid && rank < k) {
+    ids[(int64_t)t * k + rank] = lane;
+    weights[(int64_t)t * k + rank] = expf(v - m) / s;
   }
 }
 
@@ -108,14 +164,32 @@ moe_dispatch_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
       run += __popc(bits[(size_t)e * W + w]);
     }
   }
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int e = 0; e < E; ++e) {
-      offs[e] = run;
-      offsets[e] = (int32_t)run;
-      run += counts[e];
+  // expert offsets: exclusive scan of the counts by wave 0 alone (E <= 1024:
+  // lane l sums experts 16l .. 16l + 15, then a scan across the lanes)
+  if (tid < 64) {
+    const int e0 = tid * 16;
+    uint32_t c[16], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      c[i] = e0 + i < E ? counts[e0 + i] : 0u;
+      sum += c[i];
     }
-    offsets[E] = (int32_t)run;
+    uint32_t x = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off);
+      if (tid >= off) x += y;
+    }
+    uint32_t run = x - sum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (e0 + i < E) {
+        offs[e0 + i] = run;
+        offsets[e0 + i] = (int32_t)run;
+      }
+      run += c[i];
+    }
+    if (tid == 63) offsets[E] = (int32_t)x;
   }
   __syncthreads();
   for (int64_t i = tid; i < P; i += kDispatchThreads) {
@@ -192,7 +266,10 @@ hipError_t launch_moe_route(const float* logits, int64_t ld, int64_t T, int32_t 
                             int32_t* inv, hipStream_t stream) {
   if (T > 0) {
     const unsigned grid = (unsigned)((T + kRouteWaves - 1) / kRouteWaves);
-    moe_topk_kernel<<<grid, 64 * kRouteWaves, 0, stream>>>(logits, ld, (int)T, E, k, ids, weights);
+    if (E <= 64)
+      moe_topk64_kernel<<<grid, 64 * kRouteWaves, 0, stream>>>(logits, ld, (int)T, E, k, ids, weights);
+    else
+      moe_topk_kernel<<<grid, 64 * kRouteWaves, 0, stream>>>(logits, ld, (int)T, E, k, ids, weights);
   }
   const size_t lds = moe_dispatch_lds_bytes(T, E);
   const hipError_t attr = set_max_lds<&moe_dispatch_kernel>(kMoeDispatchMaxLds);
