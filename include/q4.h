@@ -324,7 +324,10 @@ q4_status q4_grouped_gemm_swiglu(const void* A_bf16, int64_t lda, int64_t T, con
  * aligned.  1 <= E <= 1024, 1 <= k <= min(E, 32), and the dispatch runs in
  * one workgroup whose LDS holds a token bitmap per expert:
  * 8*E*(ceil(T/32) + 1) bytes <= 160 KB (E = 64: T <= 10208), else
- * Q4_ERR_SHAPE.  T == 0 writes expert_offsets = 0.
+ * Q4_ERR_SHAPE.  T == 0 writes expert_offsets = 0.  Logits compare as
+ * values (-0 equal to +0); a NaN logit, outside the finite-input contract,
+ * ranks above +inf (sign bit clear) or below -inf (set), so every token
+ * still gets k distinct experts and every output index stays in range.
  */
 q4_status q4_moe_route(const float* logits, int64_t ld, int64_t T, int32_t E, int32_t k,
                        int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
