@@ -128,3 +128,25 @@ def test_relayout_scales_at_any_alignment(fmt):
     torch.cuda.synchronize()
     _same(moved, qt)
     _same(dst, qr)
+
+
+@pytest.mark.parametrize("fmt", ("mxfp4", "nvfp4"))
+def test_relayout_full_decode_weight(fmt):
+    """The 28672 x 8192 decode weight (the launch the benchmark times): both
+    directions byte-equal to the other layout's quantization, which is itself
+    checked against the oracle on sampled rows in test_gpu_quantize.py."""
+    log("relayout full", fmt)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    w = (torch.randn(28672, 8192, device=DEV, generator=g) * 0.02).bfloat16()
+    qr = q4.quantize(w, fmt, layout="rows")
+    qt = q4.quantize(w, fmt, layout="tiled")
+    del w
+    moved = q4.relayout(qr, "tiled")
+    torch.cuda.synchronize()
+    assert torch.equal(moved.codes, qt.codes) and torch.equal(moved.scales, qt.scales)
+    del moved
+    back = q4.relayout(qt, "rows")
+    torch.cuda.synchronize()
+    assert torch.equal(back.codes, qr.codes) and torch.equal(back.scales, qr.scales)
+    if fmt == "nvfp4":
+        assert torch.equal(back.global_scale, qr.global_scale)
