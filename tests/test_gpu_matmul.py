@@ -212,6 +212,31 @@ def test_full_mxfp4_decode_gemv(layout):
         log("mxfp4 decode gemv B", B, "max normalized error", e)
 
 
+@pytest.mark.parametrize("fmt", ("int4", "nvfp4", "int4_zp"))
+def test_full_decode_gemv_other_formats(fmt):
+    """The same 28672 x 8192 decode weight in the other tiled formats the
+    benchmark times, B = 1, 4, 16: 256 sampled output columns against the
+    oracle (NVFP4 under the oracle's tensor scale of the whole weight)."""
+    wl = workloads.mxfp4_gemv()
+    W = wl.tensors["W"]
+    N, K = W.shape
+    log("decode gemv: quantize", fmt)
+    qg = q4.quantize(W.to(DEV), fmt, layout="tiled")
+    rows = np.sort(np.random.default_rng(29).choice(N, 256, replace=False))
+    rows[:3] = [0, N // 2, N - 1]
+    rows = np.unique(rows)
+    gs = oracle.nv_global_scale(to_f32(W)) if fmt == "nvfp4" else None
+    wd = oracle.dequant(oracle.quantize(fmt, to_f32(W[torch.from_numpy(rows)]), gs=gs))
+    for B in (1, 4, 16):
+        x = wl.tensors[f"x{B}"]
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=DEV)
+        q4.q4_gemv(qg, x.to(DEV), y)
+        torch.cuda.synchronize()
+        e = check_matmul(y.cpu()[:, torch.from_numpy(rows)], oracle.matmul_f64(to_f32(x), wd), to_f32(x), wd,
+                         EXACT[fmt], f"{fmt} decode B={B}")
+        log(fmt, "decode gemv B", B, "max normalized error", e)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("fmt", FMTS)
 def test_strided_operands_match_contiguous(fmt, layout):
