@@ -312,3 +312,28 @@ def test_full_moe_experts_weight():
         rows = np.arange(e * N, (e + 1) * N)
         qr = oracle.quantize("mxfp4", to_f32(W[e * N:(e + 1) * N]))
         assert_quant_equal(qg, qr, "mxfp4", rows=rows)
+
+
+@pytest.mark.parametrize("fmt", ("int4", "nvfp4", "int4_zp"))
+def test_full_decode_weight_other_formats(fmt):
+    """The other formats the benchmark quantizes at 28672 x 8192 (tiled): the
+    codes and scales of 256 sampled rows, read back row-major through the
+    layout conversion, bit for bit against the oracle (NVFP4: also the
+    tensor scale, from the oracle over the whole weight)."""
+    wl = workloads.mxfp4_gemv(batches=(1,))
+    W = wl.tensors["W"]
+    N = W.shape[0]
+    log("quantize 28672x8192 tiled", fmt)
+    qg = q4.quantize(W.to(DEV), fmt, layout="tiled")
+    qrow = q4.relayout(qg, "rows")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(31).choice(N, 254, replace=False)]))
+    gs = oracle.nv_global_scale(to_f32(W)) if fmt == "nvfp4" else None
+    qr = oracle.quantize(fmt, to_f32(W[torch.from_numpy(rows)]), gs=gs)
+    sel = torch.from_numpy(rows).to(DEV)
+    codes = qrow.codes[sel].cpu().numpy()
+    scales = qrow.scales[sel].cpu().contiguous().view(torch.uint8).numpy()
+    assert np.array_equal(codes, qr.codes)
+    assert np.array_equal(scales, np.ascontiguousarray(qr.scales).view(np.uint8).reshape(scales.shape))
+    if fmt == "nvfp4":
+        assert np.float32(qg.global_scale.item()).view(np.uint32) == np.float32(gs).view(np.uint32)
