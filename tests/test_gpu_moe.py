@@ -239,3 +239,45 @@ def test_route_nan_logits_fill_every_slot(E, k):
     ref = oracle.moe_route(np.ascontiguousarray(lg[clean]), k)
     assert np.array_equal(ids_h[clean], ref.ids)
     assert np.allclose(w.cpu().numpy()[clean].astype(np.float64), ref.weights, rtol=2e-6, atol=1e-30)
+
+
+def test_full_gate_up_swiglu():
+    """The fused gate/up + SwiGLU grouped GEMM at the MoE layer the benchmark
+    times (64 experts of 2 x 2048 x 7168, MXFP4 tiled, 256 tokens, top-8, the
+    MoE workload's x and router logits): 24 sampled routed rows, all 2048
+    outputs each, against the oracle's grouped GEMM and SwiGLU for their
+    experts.  The weights are drawn as the benchmark draws them (torch's
+    generator on the GPU, N(0, 0.02^2)) and the sampled experts' bf16 rows
+    copied to the host for the oracle."""
+    E, I, K, T, k = 64, 2048, 7168, 256, 8
+    log("full gate/up swiglu: weights")
+    g = torch.Generator(device=DEV).manual_seed(5)
+    wgu = (torch.randn((E * 2 * I, K), generator=g, device=DEV) * 0.02).bfloat16()
+    qw = q4.quantize(q4.interleave_gate_up(wgu, E, I), "mxfp4", layout="tiled")
+    x = workloads.matrix("moe/A", T, K, 1.0, 0)
+    lg = workloads.normal_f32("moe/logits", T * E, 0).reshape(T, E)
+    rr = oracle.moe_route(lg, k)
+    P = T * k
+    H = torch.empty((P, I), dtype=torch.bfloat16, device=DEV)
+    q4.q4_grouped_gemm_swiglu(x.to(DEV), torch.from_numpy(rr.gather).to(DEV),
+                              torch.from_numpy(rr.offsets).to(DEV), qw, I, H)
+    torch.cuda.synchronize()
+    pick = np.unique(np.concatenate([[0, P - 1], np.random.default_rng(7).choice(P, 22, replace=False)]))
+    got = to_f32(H[torch.from_numpy(pick).to(DEV)].cpu()).astype(np.float64)
+    xa = to_f32(x)
+    expert_of = np.searchsorted(rr.offsets, pick, side="right") - 1
+    for e in np.unique(expert_of):
+        log("full gate/up swiglu: oracle, expert", int(e))
+        sel = np.nonzero(expert_of == e)[0]
+        a = xa[rr.gather[pick[sel]]]
+        wd = oracle.dequant(oracle.quantize("mxfp4", to_f32(wgu[e * 2 * I:(e + 1) * 2 * I].cpu())))
+        gu = oracle.matmul_f64(a, wd)
+        ref = oracle.swiglu(gu, I)
+        S = np.abs(a.astype(np.float64)) @ np.abs(wd.astype(np.float64)).T
+        c = 2.0 ** -16
+        gg, uu = gu[:, :I], gu[:, I:]
+        bound = (2.0 ** -8 * np.abs(ref) + 1.1 * c * (S[:, :I] * np.abs(uu) + np.abs(gg) * S[:, I:])
+                 + c * c * S[:, :I] * S[:, I:] + 1e-30)
+        err = np.abs(got[sel] - ref)
+        bad = np.argwhere(err > bound)
+        assert bad.size == 0, (int(e), [(int(i), int(j), got[sel][i, j], ref[i, j]) for i, j in bad[:5]])
